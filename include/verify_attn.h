@@ -1,0 +1,162 @@
+/*
+ * verify_attn.h — C ABI of the MI355X (gfx950) MLA tree-verify attention library.
+ *
+ * The operation: speculative-decoding verify attention for Multi-head Latent
+ * Attention. The draft tokens of a DDTree draft tree are verified against the
+ * full latent KV cache ("The Milestone Commit", Input Knowledge). The call
+ * takes the serving engine's extend layout: per sequence, the prefix's KV slot
+ * list followed by the draft tokens' slots, with the draft-token mask built
+ * over prefix + q_len positions ("The Checkpoint Report", Mistakes and
+ * Incorrect Assumptions). Here the mask is not passed in; it is derived on the
+ * device from each node's parent pointer (a node sees the whole prefix, itself
+ * and its tree ancestors).
+ *
+ * For sequence b, draft node t and head h (row r = t*H + h of the sequence):
+ *   P_b      = seq_lens[b] - T
+ *   K_j      = kv_pool[slot_idx[seg_b + j]]   (576 values: 512 latent + 64 rope)
+ *   V_j      = K_j[0:512]
+ *   visible  = every prefix key j < P_b, and the tree key P_b + u when u is t
+ *              or an ancestor of t
+ *   out[b,t,h,:] = softmax_j(sm_scale * q[b,t,h,:] . K_j) weighted sum of V_j
+ *
+ * The library is "paged + bf16 + segmented" behind a C ABI ("The Checkpoint
+ * Report", Architecture of the Report) and capture-safe: it consumes the
+ * caller's buffers, takes a caller-allocated workspace, makes no host
+ * synchronisation and no device allocation inside the call ("The Commit That
+ * Locked In 6x Decode", 1. Capture-Safe Design), so a call can be recorded in a
+ * HIP graph and replayed. The work is split over the KV sequence (split-K) and
+ * the per-split softmax partials are merged by a log-sum-exp combine ("The
+ * Milestone Commit", Thinking Process; "The Commit That Locked In 6x Decode",
+ * 2. NSPLIT=64 for TP8 Occupancy).
+ *
+ * Conventions for every entry point below:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates, frees or retains them.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously and the call returns without waiting.
+ *  - Status: 0 on success, a negative VERIFY_ATTN_ERR_* code otherwise. On an
+ *    error nothing is enqueued. No entry point prints, aborts or throws.
+ *  - Host-known parameters (the params struct) are validated on the host.
+ *    Device-resident contents (slot_idx, seq_lens, tree_parent) cannot be
+ *    checked without a host synchronisation; their validity is a
+ *    precondition. The kernels clamp every index they derive from them, so
+ *    invalid contents give meaningless output but never an out-of-bounds
+ *    access or a hang.
+ *  - The library holds no mutable global state; calls on different streams
+ *    with different workspaces may run concurrently.
+ */
+#ifndef MLA_TREE_VERIFY_ATTN_H
+#define MLA_TREE_VERIFY_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VERIFY_ATTN_KV_DIM 576   /* latent (512) + rope (64) bf16 values per KV row */
+#define VERIFY_ATTN_V_DIM 512    /* V is the first 512 values of the same row */
+#define VERIFY_ATTN_MAX_TREE 64  /* tree nodes per sequence (64-bit ancestor masks) */
+
+enum verify_attn_status {
+  VERIFY_ATTN_OK = 0,
+  VERIFY_ATTN_ERR_NULL_PTR = -1,            /* a required pointer is NULL */
+  VERIFY_ATTN_ERR_BAD_DIM = -2,             /* B/H < 1, kv_dim != 576, v_dim != 512, ... */
+  VERIFY_ATTN_ERR_TREE_TOO_LARGE = -3,      /* tree_size outside 1..64 */
+  VERIFY_ATTN_ERR_MISALIGNED = -4,          /* q/kv_pool/out/workspace not 16-byte aligned */
+  VERIFY_ATTN_ERR_WORKSPACE_TOO_SMALL = -5, /* workspace_bytes < verify_attn_workspace_size() */
+  VERIFY_ATTN_ERR_LAUNCH_FAILED = -6,       /* the HIP runtime rejected a kernel launch */
+  VERIFY_ATTN_ERR_BAD_SEQ = -7,             /* max_seq_len < tree_size, total_kv < B*T, ... */
+  VERIFY_ATTN_ERR_BAD_SPLIT = -8,           /* nsplit < 0 */
+  VERIFY_ATTN_ERR_DEVICE = -9               /* no device, or the device is not gfx950 */
+};
+
+/*
+ * Host-known shape of one call. Everything here is fixed when a call is
+ * recorded into a HIP graph; the device buffers' contents may change between
+ * replays.
+ */
+typedef struct verify_attn_params {
+  int32_t num_seqs;    /* B >= 1 sequences in the batch */
+  int32_t num_heads;   /* H >= 1 query heads (all share the one latent KV row) */
+  int32_t tree_size;   /* T in 1..64 draft-tree nodes per sequence (same T for all) */
+  int32_t kv_dim;      /* must be 576 */
+  int32_t v_dim;       /* must be 512 */
+  int32_t page_size;   /* >= 1; layout hint only (slot_idx is per token either way) */
+  int32_t max_seq_len; /* >= every seq_lens[b] and >= T; sizes the launch, no device read */
+  int32_t nsplit;      /* 0 = automatic; else the maximum number of KV splits of one sequence */
+  int64_t total_kv;    /* number of entries of slot_idx (= sum of seq_lens), >= B*T */
+  int64_t pool_slots;  /* number of rows of kv_pool, >= 1 */
+  float sm_scale;      /* softmax scale applied to q . K (e.g. 1/sqrt(192)) */
+  int32_t reserved;    /* must be 0 */
+} verify_attn_params;
+
+/*
+ * Bytes of device workspace one call needs for these params (split-K
+ * partials), or 0 when the params are invalid. The workspace is scratch: its
+ * contents need no initialisation and are meaningless after the call. Calls
+ * that may run concurrently need distinct workspaces.
+ */
+size_t verify_attn_workspace_size(const verify_attn_params* p);
+
+/*
+ * The verify attention (partial kernel, then combine kernel, on `stream`).
+ *   q           bf16 [B, T, H, 576], contiguous, 16-byte aligned
+ *   kv_pool     bf16 [pool_slots, 576], contiguous, 16-byte aligned
+ *   slot_idx    int32 [total_kv]: per sequence (in order), seq_lens[b] - T prefix
+ *               slots then the T tree nodes' own slots in node order
+ *   seq_lens    int32 [B]: P_b + T, each in [T, max_seq_len]
+ *   tree_parent int32 [B, T]: parent node of node t in [-1, t-1]; -1 = the node
+ *               hangs directly off the prefix
+ *   out         bf16 [B, T, H, 512], contiguous, 16-byte aligned (written, RNE)
+ *   workspace   >= verify_attn_workspace_size(p) bytes, 16-byte aligned
+ */
+int verify_attn(const verify_attn_params* p, const void* q, const void* kv_pool,
+                const int32_t* slot_idx, const int32_t* seq_lens, const int32_t* tree_parent,
+                void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two stages of verify_attn, separately (same arguments and checks).
+ * verify_attn_partial writes the per-split softmax partials (running max,
+ * running sum, unnormalised V sum) into the workspace; verify_attn_combine
+ * reads them and writes `out`. verify_attn == partial followed by combine.
+ * Exposed so a profiler or benchmark can time the stages on their own.
+ */
+int verify_attn_partial(const verify_attn_params* p, const void* q, const void* kv_pool,
+                        const int32_t* slot_idx, const int32_t* seq_lens,
+                        const int32_t* tree_parent, void* workspace, size_t workspace_bytes,
+                        void* stream);
+int verify_attn_combine(const verify_attn_params* p, const int32_t* seq_lens, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The launch decomposition chosen for these params (informational; the same
+ * values the calls use). Returns a status code.
+ */
+typedef struct verify_attn_plan_info {
+  int32_t rows_per_tile;   /* query rows (of H*T) per workgroup */
+  int32_t row_tiles;       /* ceil(H*T / rows_per_tile) */
+  int32_t keys_per_split;  /* KV positions per split */
+  int32_t max_splits;      /* upper bound on the total number of splits over all sequences */
+  int32_t partial_blocks;  /* workgroups of the partial kernel */
+  int32_t combine_blocks;  /* workgroups of the combine kernel */
+  int32_t threads_per_block;
+  int32_t reserved;
+} verify_attn_plan_info;
+
+int verify_attn_plan(const verify_attn_params* p, verify_attn_plan_info* info);
+
+/* Static description of a status code (never NULL). */
+const char* verify_attn_strerror(int status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int verify_attn_version(void);
+
+#define VERIFY_ATTN_VERSION ((1 << 16) | 0)
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_TREE_VERIFY_ATTN_H */

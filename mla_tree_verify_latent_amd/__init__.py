@@ -1,0 +1,217 @@
+"""Python binding of the MI355X MLA tree-verify attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libverify_attn.so`` (built from ``csrc/verify_attn.hip`` by
+``build.py``). PyTorch provides device memory and the current stream. There is
+no fallback: if the library is missing or the device is not gfx950 the calls
+raise.
+
+Entry points mirror the C ABI declared in ``include/verify_attn.h``:
+``verify_attn``, ``verify_attn_partial``, ``verify_attn_combine``,
+``verify_attn_workspace_size``, ``verify_attn_plan``, ``verify_attn_strerror``,
+``verify_attn_version``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libverify_attn.so")
+
+KV_DIM = 576
+V_DIM = 512
+MAX_TREE = 64
+
+EXPORTS = (
+    "verify_attn", "verify_attn_partial", "verify_attn_combine", "verify_attn_workspace_size",
+    "verify_attn_plan", "verify_attn_strerror", "verify_attn_version",
+)
+
+
+class Params(ctypes.Structure):
+    """Mirror of ``verify_attn_params``."""
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+        ("tree_size", ctypes.c_int32), ("kv_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+        ("nsplit", ctypes.c_int32), ("total_kv", ctypes.c_int64), ("pool_slots", ctypes.c_int64),
+        ("sm_scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+    ]
+
+
+class PlanInfo(ctypes.Structure):
+    """Mirror of ``verify_attn_plan_info``."""
+    _fields_ = [
+        ("rows_per_tile", ctypes.c_int32), ("row_tiles", ctypes.c_int32),
+        ("keys_per_split", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+        ("partial_blocks", ctypes.c_int32), ("combine_blocks", ctypes.c_int32),
+        ("threads_per_block", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class VerifyAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"verify_attn status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load (once) and return the ctypes handle of libverify_attn.so."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m mla_tree_verify_latent_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    P, vp, i32p = ctypes.POINTER(Params), ctypes.c_void_p, ctypes.c_void_p
+    lib.verify_attn_workspace_size.argtypes = [P]
+    lib.verify_attn_workspace_size.restype = ctypes.c_size_t
+    lib.verify_attn.argtypes = [P, vp, vp, i32p, i32p, i32p, vp, vp, ctypes.c_size_t, vp]
+    lib.verify_attn.restype = ctypes.c_int
+    lib.verify_attn_partial.argtypes = [P, vp, vp, i32p, i32p, i32p, vp, ctypes.c_size_t, vp]
+    lib.verify_attn_partial.restype = ctypes.c_int
+    lib.verify_attn_combine.argtypes = [P, i32p, vp, vp, ctypes.c_size_t, vp]
+    lib.verify_attn_combine.restype = ctypes.c_int
+    lib.verify_attn_plan.argtypes = [P, ctypes.POINTER(PlanInfo)]
+    lib.verify_attn_plan.restype = ctypes.c_int
+    lib.verify_attn_strerror.argtypes = [ctypes.c_int]
+    lib.verify_attn_strerror.restype = ctypes.c_char_p
+    lib.verify_attn_version.argtypes = []
+    lib.verify_attn_version.restype = ctypes.c_int
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def make_params(*, num_seqs: int, num_heads: int, tree_size: int, max_seq_len: int,
+                total_kv: int, pool_slots: int, sm_scale: float, nsplit: int = 0,
+                page_size: int = 1, kv_dim: int = KV_DIM, v_dim: int = V_DIM) -> Params:
+    return Params(num_seqs, num_heads, tree_size, kv_dim, v_dim, page_size, max_seq_len, nsplit,
+                  total_kv, pool_slots, sm_scale, 0)
+
+
+def verify_attn_strerror(status: int) -> str:
+    return load_library().verify_attn_strerror(int(status)).decode()
+
+
+def verify_attn_version() -> int:
+    return int(load_library().verify_attn_version())
+
+
+def verify_attn_workspace_size(params: Params) -> int:
+    return int(load_library().verify_attn_workspace_size(ctypes.byref(params)))
+
+
+def verify_attn_plan(params: Params) -> dict:
+    info = PlanInfo()
+    _check(load_library().verify_attn_plan(ctypes.byref(params), ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in PlanInfo._fields_ if name != "reserved"}
+
+
+def _check(status: int):
+    if status != 0:
+        raise VerifyAttnError(status, verify_attn_strerror(status))
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _check_tensors(q, kv_pool, slot_idx, seq_lens, tree_parent, out=None):
+    import torch
+    named = dict(q=q, kv_pool=kv_pool, slot_idx=slot_idx, seq_lens=seq_lens,
+                 tree_parent=tree_parent)
+    if out is not None:
+        named["out"] = out
+    for name, t in named.items():
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name in ("q", "kv_pool") + (("out",) if out is not None else ()):
+        if named[name].dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    for name in ("slot_idx", "seq_lens", "tree_parent"):
+        if named[name].dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    if q.dim() != 4 or q.shape[-1] != KV_DIM:
+        raise ValueError("q must be [B, T, H, 576]")
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != KV_DIM:
+        raise ValueError("kv_pool must be [slots, 576]")
+    B, T, H, _ = q.shape
+    if tuple(seq_lens.shape) != (B,) or tuple(tree_parent.shape) != (B, T):
+        raise ValueError("seq_lens must be [B] and tree_parent [B, T]")
+    if out is not None and tuple(out.shape) != (B, T, H, V_DIM):
+        raise ValueError("out must be [B, T, H, 512]")
+
+
+def params_for(q, kv_pool, slot_idx, *, max_seq_len: int, sm_scale: float, nsplit: int = 0,
+               page_size: int = 1) -> Params:
+    """Params of a call on these tensors. max_seq_len is host-known by the caller."""
+    B, T, H, _ = q.shape
+    return make_params(num_seqs=B, num_heads=H, tree_size=T, max_seq_len=int(max_seq_len),
+                       total_kv=int(slot_idx.numel()), pool_slots=int(kv_pool.shape[0]),
+                       sm_scale=float(sm_scale), nsplit=int(nsplit), page_size=int(page_size))
+
+
+def verify_attn(q, kv_pool, slot_idx, seq_lens, tree_parent, out, workspace, params: Params,
+                stream=None) -> None:
+    """Enqueue the verify attention on `stream` (default: torch's current stream)."""
+    _check_tensors(q, kv_pool, slot_idx, seq_lens, tree_parent, out)
+    _check(load_library().verify_attn(
+        ctypes.byref(params), _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
+        _ptr(tree_parent), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def verify_attn_partial(q, kv_pool, slot_idx, seq_lens, tree_parent, workspace, params: Params,
+                        stream=None) -> None:
+    _check_tensors(q, kv_pool, slot_idx, seq_lens, tree_parent)
+    _check(load_library().verify_attn_partial(
+        ctypes.byref(params), _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
+        _ptr(tree_parent), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def verify_attn_combine(seq_lens, out, workspace, params: Params, stream=None) -> None:
+    _check(load_library().verify_attn_combine(
+        ctypes.byref(params), _ptr(seq_lens), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+class VerifyAttention:
+    """A call shape with its workspace allocated once (torch, on the device).
+
+    ``__call__`` makes no allocation other than ``out`` when it is not given,
+    so with ``out`` passed in it can be captured in a HIP graph.
+    """
+
+    def __init__(self, params: Params, device="cuda"):
+        import torch
+        self.params = params
+        nbytes = verify_attn_workspace_size(params)
+        if nbytes == 0:
+            raise ValueError("invalid verify_attn params")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+    def __call__(self, q, kv_pool, slot_idx, seq_lens, tree_parent, out=None, stream=None):
+        import torch
+        if out is None:
+            B, T, H, _ = q.shape
+            out = torch.empty((B, T, H, V_DIM), dtype=torch.bfloat16, device=q.device)
+        verify_attn(q, kv_pool, slot_idx, seq_lens, tree_parent, out, self.workspace, self.params,
+                    stream)
+        return out

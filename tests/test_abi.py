@@ -1,0 +1,126 @@
+"""The C-ABI library loads, exports what include/verify_attn.h declares, and
+rejects host-detectable errors with the documented codes (no GPU work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_tree_verify_latent_amd as mtv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "verify_attn.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(verify_attn\w*)\s*\(", text)))
+
+
+def header_enum(name):
+    text = open(HEADER).read()
+    m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
+    return int(m.group(1))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mtv.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(mtv.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+
+
+def test_version(lib):
+    assert mtv.verify_attn_version() == (1 << 16)
+
+
+def base_params(**kw):
+    d = dict(num_seqs=1, num_heads=8, tree_size=64, max_seq_len=65600, total_kv=65600,
+             pool_slots=131072, sm_scale=0.0721, nsplit=0)
+    d.update(kw)
+    return mtv.make_params(**d)
+
+
+def test_workspace_and_plan():
+    p = base_params()
+    ws = mtv.verify_attn_workspace_size(p)
+    plan = mtv.verify_attn_plan(p)
+    M = 8 * 64
+    assert plan["row_tiles"] == -(-M // plan["rows_per_tile"])
+    assert plan["keys_per_split"] % 32 == 0
+    assert plan["max_splits"] >= -(-65600 // plan["keys_per_split"])
+    assert plan["partial_blocks"] % 8 == 0
+    assert plan["partial_blocks"] >= plan["max_splits"] * plan["row_tiles"]
+    assert ws == plan["max_splits"] * M * (512 + 2) * 4
+    # nsplit fixes the split length from max_seq_len
+    p1 = base_params(nsplit=1)
+    assert mtv.verify_attn_plan(p1)["keys_per_split"] >= 65600
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_seqs", 0, "VERIFY_ATTN_ERR_BAD_DIM"),
+    ("num_heads", 0, "VERIFY_ATTN_ERR_BAD_DIM"),
+    ("kv_dim", 512, "VERIFY_ATTN_ERR_BAD_DIM"),
+    ("v_dim", 576, "VERIFY_ATTN_ERR_BAD_DIM"),
+    ("tree_size", 0, "VERIFY_ATTN_ERR_TREE_TOO_LARGE"),
+    ("tree_size", 65, "VERIFY_ATTN_ERR_TREE_TOO_LARGE"),
+    ("max_seq_len", 63, "VERIFY_ATTN_ERR_BAD_SEQ"),
+    ("total_kv", 63, "VERIFY_ATTN_ERR_BAD_SEQ"),
+    ("total_kv", 65601, "VERIFY_ATTN_ERR_BAD_SEQ"),
+    ("nsplit", -1, "VERIFY_ATTN_ERR_BAD_SPLIT"),
+    ("pool_slots", 0, "VERIFY_ATTN_ERR_BAD_DIM"),
+    ("page_size", 0, "VERIFY_ATTN_ERR_BAD_DIM"),
+    ("reserved", 1, "VERIFY_ATTN_ERR_BAD_DIM"),
+])
+def test_param_errors(lib, field, value, code):
+    p = base_params()
+    setattr(p, field, value)
+    assert mtv.verify_attn_workspace_size(p) == 0
+    fake = 1 << 20
+    rc = lib.verify_attn(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, 1 << 40, None)
+    assert rc == header_enum(code)
+    assert mtv.verify_attn_strerror(rc) not in ("ok", "unknown status")
+
+
+def test_pointer_errors(lib):
+    p = base_params()
+    ws = mtv.verify_attn_workspace_size(p)
+    a = 1 << 20
+    args = [a, a, a, a, a, a, a]
+    for i in range(7):
+        bad = list(args)
+        bad[i] = None
+        rc = lib.verify_attn(ctypes.byref(p), *bad, ws, None)
+        assert rc == header_enum("VERIFY_ATTN_ERR_NULL_PTR"), i
+    for i in (0, 1, 5, 6):  # q, kv_pool, out, workspace must be 16-byte aligned
+        bad = list(args)
+        bad[i] = a + 8
+        rc = lib.verify_attn(ctypes.byref(p), *bad, ws, None)
+        assert rc == header_enum("VERIFY_ATTN_ERR_MISALIGNED"), i
+    rc = lib.verify_attn(ctypes.byref(p), *args, ws - 1, None)
+    assert rc == header_enum("VERIFY_ATTN_ERR_WORKSPACE_TOO_SMALL")
+    rc = lib.verify_attn(None, *args, ws, None)
+    assert rc == header_enum("VERIFY_ATTN_ERR_NULL_PTR")
+
+
+def test_no_device_here(lib):
+    """Valid arguments on a host without a gfx950 device: ERR_DEVICE, nothing launched."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a device is present; this checks the no-device path only")
+    p = base_params()
+    ws = mtv.verify_attn_workspace_size(p)
+    a = 1 << 20
+    rc = lib.verify_attn(ctypes.byref(p), a, a, a, a, a, a, a, ws, None)
+    assert rc == header_enum("VERIFY_ATTN_ERR_DEVICE")
+
+
+def test_strerror_total(lib):
+    for code in range(-12, 2):
+        assert isinstance(mtv.verify_attn_strerror(code), str)

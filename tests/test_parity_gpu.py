@@ -1,0 +1,232 @@
+"""HIP path vs the CPU oracle on identical seeded inputs (needs a gfx950 GPU).
+
+Gate (per output row (b, t, h)): max_d |gpu - oracle| <= 2 bf16 ULP of
+max_d |oracle|. The oracle is fp64; the GPU output is bf16 (RNE) of an fp32
+online softmax with bf16 MFMA operands (q, K, V exact; P rounded to bf16).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import parity_gate, run_gpu, sample_rows, to_device, params_of, bf16_out_to_f32
+from synthetic import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_tree_verify_latent_amd as mtv
+    mtv.load_library()
+    return torch.device("cuda")
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.load()
+
+
+def check_full(orc, wl, nsplit=0, ulps=2.0):
+    got = run_gpu(wl, nsplit)
+    ref = orc.run(wl)
+    ok, worst, idx = parity_gate(got, ref, ulps)
+    assert ok, f"{wl.name}: worst row {idx} at {worst:.2f} bf16 ulp"
+    return got, ref
+
+
+def check_sampled(orc, wl, n_per_seq=24, nsplit=0, dev=None):
+    got = run_gpu(wl, nsplit, dev)
+    rows = sample_rows(wl, n_per_seq)
+    ref = orc.run_rows(wl, rows)
+    g = np.stack([got[b, t, h] for b, t, h in rows])
+    ok, worst, idx = parity_gate(g, ref)
+    assert ok, f"{wl.name}: row {tuple(rows[idx])} at {worst:.2f} bf16 ulp"
+    return got
+
+
+def small(name="small", B=1, H=8, T=8, prefixes=(256,), pool=None, seed=11, **kw):
+    prefixes = list(prefixes)
+    if pool is None:
+        pool = sum(prefixes) + B * T + 101
+    return inputs.make_workload(name, B=B, H=H, T=T, prefixes=prefixes, pool_slots=pool,
+                                seed=seed, **kw)
+
+
+# ------------------------------------------------------------ configurations
+
+def test_c1_tiny_full(orc):
+    check_full(orc, inputs.config("c1_tiny"))
+
+
+def test_c2_tp_share_full(orc):
+    check_full(orc, inputs.config("c2_tp_share"))
+
+
+def test_c3_full_head_sampled(orc):
+    check_sampled(orc, inputs.config("c3_full_head"), n_per_seq=48)
+
+
+def test_c4_long_both_layouts(orc):
+    a = inputs.config("c4a_long_scattered")
+    got_a = check_sampled(orc, a, n_per_seq=32)
+    b = inputs.config("c4b_long_contiguous")
+    got_b = run_gpu(b)
+    assert np.array_equal(got_a, got_b), "layouts (a) and (b) hold the same values"
+
+
+def test_c5_ragged_sampled(orc):
+    check_sampled(orc, inputs.config("c5_ragged"), n_per_seq=16)
+
+
+def test_e2_production_shape_sampled(orc):
+    check_sampled(orc, inputs.config("e2_h8_t9_65k"), n_per_seq=32)
+
+
+# ------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("case", [
+    dict(B=1, H=1, T=1, prefixes=[0]),                 # single key: out == own V row
+    dict(B=1, H=3, T=5, prefixes=[7]),                 # M=15 rows, ragged everything
+    dict(B=3, H=2, T=7, prefixes=[0, 33, 95]),         # ragged batch, P=0 included
+    dict(B=2, H=8, T=64, prefixes=[31, 64]),           # full tree size
+    dict(B=1, H=64, T=3, prefixes=[1000]),             # 192 rows, 3 row tiles
+    dict(B=1, H=16, T=9, prefixes=[4097]),             # tail tile of 1 key + tree
+    dict(B=4, H=8, T=16, prefixes=[5000, 1, 32, 2047]),
+], ids=lambda c: "B{B}_H{H}_T{T}_P{prefixes}".format(**c))
+def test_edge_shapes(orc, case):
+    check_full(orc, small(**case))
+
+
+@pytest.mark.parametrize("tree", ["flat", "chain"])
+def test_tree_shapes(orc, tree):
+    check_full(orc, small(H=4, T=64, prefixes=[300], tree=tree, seed=5))
+
+
+def test_single_key_exact():
+    wl = small(B=2, H=4, T=1, prefixes=[0, 0], seed=3)
+    got = run_gpu(wl)
+    v = inputs.bf16_bits_to_f32(wl.kv_pool[wl.slot_idx])[:, :512]
+    for b in range(2):
+        for h in range(4):
+            assert np.array_equal(got[b, 0, h], v[b])
+
+
+@pytest.mark.parametrize("nsplit", [1, 2, 7, 64, 0])
+def test_nsplit_independent(orc, nsplit):
+    wl = inputs.config("c2_tp_share")
+    check_full(orc, wl, nsplit=nsplit)
+
+
+def test_zero_query_is_mean(orc):
+    wl = small(H=2, T=12, prefixes=[500], seed=8)
+    wl.q[:] = 0
+    check_full(orc, wl)
+
+
+def test_constant_column():
+    wl = small(H=4, T=8, prefixes=[777], seed=9)
+    c = inputs.f32_to_bf16_bits(np.array([0.375], np.float32))[0]
+    wl.kv_pool[:, 100] = c
+    got = run_gpu(wl)
+    assert np.all(got[..., 100] == np.float32(0.375))
+
+
+def test_slot_permutation_bitwise():
+    wl = small(B=2, H=8, T=8, prefixes=[900, 300], pool=4096, seed=12)
+    got = run_gpu(wl)
+    rng = np.random.default_rng(1)
+    pi = rng.permutation(wl.pool_slots)
+    pool = np.empty_like(wl.kv_pool)
+    pool[pi] = wl.kv_pool
+    wl.kv_pool = pool
+    wl.slot_idx = pi[wl.slot_idx].astype(np.int32)
+    assert np.array_equal(run_gpu(wl), got)
+
+
+def test_head_subset_bitwise():
+    wl64 = small(H=64, T=8, prefixes=[2000], seed=13)
+    got64 = run_gpu(wl64, nsplit=4)
+    wl8 = small(H=64, T=8, prefixes=[2000], seed=13)
+    wl8.H = 8
+    wl8.q = np.ascontiguousarray(wl64.q[:, :, :8])
+    got8 = run_gpu(wl8, nsplit=4)
+    assert np.array_equal(got8, got64[:, :, :8])
+
+
+def test_deterministic():
+    wl = inputs.config("c2_tp_share")
+    dev = to_device(wl)
+    a = run_gpu(wl, dev=dev)
+    b = run_gpu(wl, dev=dev)
+    assert np.array_equal(a, b)
+
+
+def test_graph_capture_replay():
+    """The call records into a HIP graph; replays match eager, with inputs changed between."""
+    import torch
+    import mla_tree_verify_latent_amd as mtv
+    wl = small(B=2, H=8, T=16, prefixes=[3000, 1200], seed=14)
+    dev = to_device(wl)
+    op = mtv.VerifyAttention(params_of(wl))
+    out = torch.empty((wl.B, wl.T, wl.H, 512), dtype=torch.bfloat16, device="cuda")
+    op(**dev, out=out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        op(**dev, out=out)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        op(**dev, out=out)
+    q0 = dev["q"].clone()
+    for rep in range(4):
+        out.zero_()
+        if rep % 2:
+            dev["q"].copy_(torch.flip(q0, dims=[1]))
+        else:
+            dev["q"].copy_(q0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if rep % 2:
+            ref = torch.empty_like(out)
+            op(**dev, out=ref)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), rep
+        else:
+            assert torch.equal(out, eager), rep
+
+
+def test_stage_entry_points_match_full_call():
+    import torch
+    import mla_tree_verify_latent_amd as mtv
+    wl = small(B=2, H=8, T=8, prefixes=[1500, 700], seed=15)
+    dev = to_device(wl)
+    prm = params_of(wl)
+    op = mtv.VerifyAttention(prm)
+    full = op(**dev)
+    out = torch.empty_like(full)
+    mtv.verify_attn_partial(dev["q"], dev["kv_pool"], dev["slot_idx"], dev["seq_lens"],
+                            dev["tree_parent"], op.workspace, prm)
+    mtv.verify_attn_combine(dev["seq_lens"], out, op.workspace, prm)
+    torch.cuda.synchronize()
+    assert torch.equal(out, full)
+
+
+def test_host_errors_raise_without_launch():
+    import torch
+    import mla_tree_verify_latent_amd as mtv
+    wl = small(seed=16)
+    dev = to_device(wl)
+    prm = params_of(wl)
+    ws = torch.empty(mtv.verify_attn_workspace_size(prm) - 16, dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, 8, 8, 512), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mtv.VerifyAttnError) as e:
+        mtv.verify_attn(**dev, out=out, workspace=ws, params=prm)
+    assert e.value.status == -5
