@@ -1,0 +1,298 @@
+"""Benchmark of MLA tree-verify attention on one MI355X.
+
+A step is one verify_attn call (partial kernel + combine kernel) over one
+batch of synthetic input resident in HBM. The headline workload is the
+long-context H=8 configuration at 65k context (one sequence, prefix 65,536,
+64-node draft tree, page_size=1 scattered slots in a 131,072-slot pool). The
+H=64 point at 65k (the ragged 4-sequence batch whose sequences run 4k..200k)
+and the other 65k points are reported beside it.
+
+Timing: every step reads its own replica of (pool, q) from a rotation whose
+total KV bytes exceed twice the 256 MB Infinity Cache, so repeats are served
+from HBM; the K timed steps are recorded in one HIP graph and replayed once,
+bracketed by synchronisation, and timed with HIP events on the launch stream.
+The partial kernel is also timed on its own the same way: that duration gives
+the roofline figure.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+MALL_BYTES = 256 << 20
+KV_ROW_BYTES = 576 * 2
+FLOPS_PER_KEY_ROW = 2 * 576 + 2 * 512  # QK^T + PV per (KV row, query row)
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_partial_c4a.json")
+KERNEL_SRC = os.path.join(ROOT, "mla_tree_verify_latent_amd", "csrc", "verify_attn.hip")
+
+WORKLOAD_TEXT = {
+    "c4a_long_scattered": "long-context verify: H=8, 1 sequence, prefix 65536, T=64, page_size=1 "
+                          "scattered in a 131072-slot bf16 [slots, 576] pool",
+    "c4b_long_contiguous": "long-context verify, defragmented: same values, page_size=64 contiguous",
+    "c5_ragged": "ragged batched long-context: H=64, 4 sequences, prefixes 4096/23552/65536/200704, "
+                 "T=64 each, shared 300000-slot pool, scattered",
+    "e1_h64_65k": "full-head 65k: H=64, 1 sequence, prefix 65536, T=64, scattered",
+    "e2_h8_t9_65k": "production shape: H=8, 1 sequence, prefix 65536, T=9, scattered",
+    "c2_tp_share": "TP-share decode verify: H=8, prefix 4096, T=32, 65536-slot pool",
+    "c3_full_head": "full-head verify: H=64, prefix 16384, T=32, 131072-slot pool",
+}
+
+
+def algorithmic_bytes(wl) -> int:
+    """Bytes one call must move at least: each referenced KV row and its slot index once,
+    q and out once, the tree and the sequence lengths once."""
+    rows = wl.total_kv
+    return (rows * (KV_ROW_BYTES + 4) + wl.B * wl.T * wl.H * (576 + 512) * 2
+            + wl.B * wl.T * 4 + wl.B * 4)
+
+
+def algorithmic_flops(wl) -> int:
+    """2*(576 + 512) flops per (KV row, query row) pair of the same sequence."""
+    return int(wl.seq_lens.astype(np.int64).sum()) * wl.H * wl.T * FLOPS_PER_KEY_ROW
+
+
+def kernel_source_digest() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+class Bench:
+    """Device copies of one workload, R replicas, and graph-timed runs."""
+
+    def __init__(self, wl, replicas: int, nsplit: int = 0):
+        import torch
+        import mla_tree_verify_latent_amd as mtv
+        from synthetic.device import to_device, params_of
+        self.torch, self.mtv, self.wl = torch, mtv, wl
+        base = to_device(wl)
+        self.params = params_of(wl, nsplit)
+        self.ws = torch.empty(mtv.verify_attn_workspace_size(self.params), dtype=torch.uint8,
+                              device="cuda")
+        self.reps = []
+        for r in range(replicas):
+            d = dict(base)
+            if r:
+                d["kv_pool"] = base["kv_pool"].clone()
+                d["q"] = base["q"].clone()
+            self.reps.append(d)
+        self.out = torch.empty((wl.B, wl.T, wl.H, 512), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+
+    def call(self, r, stage="full"):
+        d = self.reps[r % len(self.reps)]
+        if stage == "full":
+            self.mtv.verify_attn(d["q"], d["kv_pool"], d["slot_idx"], d["seq_lens"],
+                                 d["tree_parent"], self.out, self.ws, self.params)
+        elif stage == "partial":
+            self.mtv.verify_attn_partial(d["q"], d["kv_pool"], d["slot_idx"], d["seq_lens"],
+                                         d["tree_parent"], self.ws, self.params)
+        elif stage == "combine":
+            self.mtv.verify_attn_combine(d["seq_lens"], self.out, self.ws, self.params)
+
+    def graph(self, n, stage):
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.call(0, stage)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                self.call(i, stage)
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(self, steps, warmup, stage="full", repeats=3):
+        """Median over `repeats` replays of a graph of `steps` calls; ms per call."""
+        torch = self.torch
+        if warmup:
+            gw = self.graph(warmup, stage)
+            gw.replay()
+            torch.cuda.synchronize()
+        g = self.graph(steps, stage)
+        times = []
+        for _ in range(repeats):
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record()
+            g.replay()
+            end.record()
+            torch.cuda.synchronize()
+            times.append(start.elapsed_time(end) / steps)
+        return statistics.median(times), times
+
+
+def replicas_for(wl) -> int:
+    return max(1, math.ceil(2 * MALL_BYTES / max(1, wl.kv_bytes())))
+
+
+def measure(name, steps, warmup, nsplit=0, stages=("full", "partial")):
+    from synthetic import inputs
+    wl = inputs.config(name)
+    R = replicas_for(wl)
+    b = Bench(wl, R, nsplit)
+    res = {"workload": name, "replicas": R, "plan": b.mtv.verify_attn_plan(b.params)}
+    for st in stages:
+        ms, all_ms = b.time_graph(steps, warmup, st)
+        res[f"{st}_ms"] = ms
+        res[f"{st}_ms_repeats"] = all_ms
+    warm = Bench(wl, 1, nsplit)
+    res["full_ms_mall_warm"], _ = warm.time_graph(steps, warmup, "full")
+    res["bytes"] = algorithmic_bytes(wl)
+    res["flops"] = algorithmic_flops(wl)
+    res["wl"] = wl
+    del b, warm
+    return res
+
+
+def cpu_baseline(name, repeats=3):
+    """The oracle (fp64 C, OpenMP) on whole calls of the same workload."""
+    import oracle
+    from synthetic import inputs
+    wl = inputs.config(name)
+    orc = oracle.load()
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        orc.run(wl)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {
+        "value": algorithmic_bytes(wl) / t / 1e9, "unit": "GB/s", "cores": orc.num_threads(),
+        "kind": "oracle",
+        "sample": f"{name}: whole call ({wl.B * wl.T * wl.H} output rows), median of {repeats} "
+                  f"calls, {t:.2f} s per call",
+        "s_per_call": t,
+    }
+
+
+def traffic_from_counters(partial_ms):
+    """HBM bytes per partial launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counters (scaled by a copy-kernel calibration), if they were taken on this source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    c = json.load(open(COUNTERS_FILE))
+    if c.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    return c["hbm_bytes_per_launch"]
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c4a_long_scattered")
+    ap.add_argument("--extras", default="e1_h64_65k,c5_ragged,c4b_long_contiguous,e2_h8_t9_65k",
+                    help="comma-separated extra workloads reported beside the headline ('' = none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage", default=None, choices=[None, "full", "partial", "combine"],
+                    help="profiling aid: only run K calls of one stage of the headline workload")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the verify path has no multi-GPU mode "
+              "(heads, sequences or KV positions would shard across GPUs; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import mla_tree_verify_latent_amd as mtv
+    mtv.load_library()
+
+    if args.stage:
+        from synthetic import inputs
+        wl = inputs.config(args.workload)
+        b = Bench(wl, replicas_for(wl))
+        for i in range(args.warmup + args.steps):
+            b.call(i, args.stage)
+        torch.cuda.synchronize()
+        print(json.dumps({"stage": args.stage, "workload": args.workload, "calls": args.warmup + args.steps}))
+        return
+
+    head = measure(args.workload, args.steps, args.warmup)
+    ms = head["full_ms"]
+    gbs = head["bytes"] / (ms * 1e-3) / 1e9
+    part_ms = head["partial_ms"]
+    part_tflops = head["flops"] / (part_ms * 1e-3) / 1e12
+    extras = {}
+    for name in [e for e in args.extras.split(",") if e]:
+        r = measure(name, max(10, args.steps // 4), max(2, args.warmup // 4))
+        extras[name] = {
+            "workload": WORKLOAD_TEXT.get(name, name),
+            "ms_per_call": round(r["full_ms"], 5),
+            "calls_per_s": round(1e3 / r["full_ms"], 1),
+            "hbm_gbs": round(r["bytes"] / (r["full_ms"] * 1e-3) / 1e9, 1),
+            "hbm_frac": round(r["bytes"] / (r["full_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "partial_ms": round(r["partial_ms"], 5),
+            "partial_mfma_tflops": round(r["flops"] / (r["partial_ms"] * 1e-3) / 1e12, 1),
+            "mfma_frac": round(r["flops"] / (r["partial_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "ms_per_call_mall_warm": round(r["full_ms_mall_warm"], 5),
+            "replicas": r["replicas"],
+        }
+        torch.cuda.empty_cache()
+
+    line = {
+        "metric": "achieved HBM GB/s (% of peak) + verify calls/sec at 65k ctx, H=8 and H=64",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_TEXT[args.workload],
+            "name": args.workload,
+            "num_seqs": head["wl"].B, "heads": head["wl"].H, "tree_nodes": head["wl"].T,
+            "prefix": head["wl"].prefixes, "pool_slots": head["wl"].pool_slots,
+            "plan": head["plan"], "replicas": head["replicas"],
+        },
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "calls_per_s": round(1e3 / ms, 1),
+        "ms_per_call_mall_warm": round(head["full_ms_mall_warm"], 5),
+        "partial_kernel_ms": round(part_ms, 5),
+        "combine_share": round(1.0 - part_ms / ms, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(part_tflops, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(part_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_from_counters(part_ms),
+        },
+        "extras": extras,
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(args.workload)
+        line["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                for k, v in cb.items() if k != "s_per_call"}
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

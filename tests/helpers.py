@@ -25,23 +25,7 @@ def parity_gate(got: np.ndarray, ref: np.ndarray, ulps: float = 2.0):
     return bool((ratio <= 1.0).all()), float(ratio[worst] * ulps), worst
 
 
-def to_device(wl, device="cuda"):
-    import torch
-    return dict(
-        q=torch.from_numpy(wl.q.view(np.int16)).view(torch.bfloat16).to(device),
-        kv_pool=torch.from_numpy(wl.kv_pool.view(np.int16)).view(torch.bfloat16).to(device),
-        slot_idx=torch.from_numpy(wl.slot_idx).to(device),
-        seq_lens=torch.from_numpy(wl.seq_lens).to(device),
-        tree_parent=torch.from_numpy(wl.tree_parent).to(device),
-    )
-
-
-def params_of(wl, nsplit: int = 0):
-    import mla_tree_verify_latent_amd as mtv
-    return mtv.make_params(num_seqs=wl.B, num_heads=wl.H, tree_size=wl.T,
-                           max_seq_len=wl.max_seq_len, total_kv=wl.total_kv,
-                           pool_slots=wl.pool_slots, sm_scale=wl.sm_scale, nsplit=nsplit,
-                           page_size=wl.page_size)
+from synthetic.device import params_of, to_device  # noqa: E402,F401
 
 
 def run_gpu(wl, nsplit: int = 0, dev=None) -> np.ndarray:
