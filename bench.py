@@ -203,8 +203,9 @@ def main():
     ap.add_argument("--extras", default="e1_h64_65k,c5_ragged,c4b_long_contiguous,e2_h8_t9_65k",
                     help="comma-separated extra workloads reported beside the headline ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stage", default=None, choices=[None, "full", "partial", "combine"],
-                    help="profiling aid: only run K calls of one stage of the headline workload")
+    ap.add_argument("--stage", default=None, choices=[None, "full", "partial", "combine", "copy"],
+                    help="profiling aid: only run K calls of one stage of the headline workload; "
+                         "'copy' runs K device-to-device copies of 1 GiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -220,6 +221,16 @@ def main():
     import mla_tree_verify_latent_amd as mtv
     mtv.load_library()
 
+    if args.stage == "copy":
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"stage": "copy", "bytes_read_per_copy": src.numel() * 4,
+                          "bytes_written_per_copy": dst.numel() * 4, "copies": args.steps}))
+        return
     if args.stage:
         from synthetic import inputs
         wl = inputs.config(args.workload)

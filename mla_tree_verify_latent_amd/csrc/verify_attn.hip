@@ -39,23 +39,27 @@ constexpr int V_DIM = 512;
 constexpr int MAX_TREE = 64;
 
 // Partial kernel geometry.
-constexpr int NW = 4;                      // waves per workgroup
-constexpr int ROWS_PER_WAVE = 16;          // query rows per wave (MFMA N for QK, N for PV)
-constexpr int ROWS_PER_TILE = NW * ROWS_PER_WAVE;  // 64
+constexpr int NWAVES = 8;                  // waves per workgroup (two per SIMD)
+constexpr int ROWS_PER_WAVE = 16;          // query rows per wave (MFMA N for QK and PV)
+constexpr int ROWS_PER_TILE = NWAVES * ROWS_PER_WAVE;  // 128 query rows per workgroup
 constexpr int NK = 32;                     // KV rows per LDS tile
-constexpr int ROWS_PER_WAVE_LOAD = NK / NW;  // 8 KV rows loaded by each wave
+constexpr int LOAD_WAVES = 4;              // waves that gather the KV tiles
+constexpr int ROWS_PER_LOAD_WAVE = NK / LOAD_WAVES;  // 8 KV rows per loading wave
 constexpr int CHUNK_GROUPS = KV_DIM / 64;  // 9 groups of 64 bf16 (8 x 16 B) per KV row
 constexpr int GROUP_BYTES = NK * 128;      // one group for all NK rows: 4 KB
 constexpr int TILE_BYTES = CHUNK_GROUPS * GROUP_BYTES;  // 36 KB
+constexpr int NBUF = 4;                    // LDS ring of KV tiles (144 KB)
+constexpr int PREFETCH = NBUF - 1;         // tiles in flight beyond the one in use
 constexpr int QK_STEPS = KV_DIM / 32;      // 18 MFMA k-steps of 32 features
 constexpr int PV_BLOCKS = V_DIM / 16;      // 32 output blocks of 16 features
 constexpr float LAZY_RESCALE_LOG2 = 8.0f;  // running max is raised only past +8 (base 2)
-
-constexpr int COMBINE_ROWS_PER_BLOCK = 4;  // one wave per output row
+constexpr int QK_AHEAD = 4;                // K operand reads in flight ahead of their MFMA
+constexpr int PV_AHEAD = 4;                // V^T operand reads (pairs) in flight ahead
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -65,6 +69,7 @@ struct Plan {
   int chunk;           // keys per split (multiple of NK)
   int max_splits;      // bound on the total number of splits
   int partial_blocks;  // multiple of 8
+  int combine_wpr;     // waves per output row in the combine kernel (1, 4 or 16)
   int combine_blocks;
   size_t part_o_bytes;
   size_t ws_bytes;
@@ -149,10 +154,17 @@ __device__ bool locate_split(const int32_t* __restrict__ seq_lens, int B, int T,
   return false;
 }
 
-// Swizzle of the 16-byte chunk position inside a 128-byte row segment, so that
-// the MFMA operand reads (8 consecutive KV rows, same column) and the
-// transpose reads (4 rows x 2 chunks) hit distinct LDS bank groups.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// Swizzle of the 16-byte chunk position inside a 128-byte row segment. The LDS
+// serves 256 bytes per clock (64 banks x 4 bytes = 16 chunk slots); a chunk at
+// byte address A sits in slot (A / 16) % 16 = 8 * (row & 1) + position, with
+// position = (c % 8) ^ swz(row). Both access patterns of the kernel are then
+// conflict-free:
+//  - MFMA operand reads (ds_read_b128; 16 lanes = 16 consecutive KV rows, one
+//    chunk): over the 8 rows of one parity swz is a bijection of 0..7;
+//  - transpose reads (ds_read_b64_tr_b16; 32 lanes = 4 consecutive rows from a
+//    multiple of 4, times 4 consecutive chunks from a multiple of 4): the two
+//    rows of one parity differ in bit 2 of swz, so their chunk sets never meet.
+__device__ __forceinline__ int swz(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt in
 // 6:4, lgkmcnt in 11:8. A field at its maximum does not wait.
@@ -210,6 +222,21 @@ __device__ __forceinline__ void load_to_lds16(const void* gptr, uint32_t lds_bas
 }
 #pragma clang diagnostic pop
 
+// Value of lane l ^ 16 / l ^ 32 (gfx950 permlane swaps; plain VALU, no LDS).
+__device__ __forceinline__ float xor16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  // r[0]: odd 16-lane rows replaced by the even rows of the source; r[1]: even
+  // rows replaced by the odd rows. Lane l's partner l ^ 16 is in r[1] for even
+  // rows and in r[0] for odd rows.
+  return __builtin_bit_cast(float, ((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, ((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   u += 0x7fffu + ((u >> 16) & 1u);
@@ -218,20 +245,34 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 // ------------------------------------------------------------ partial kernel
 //
-// LDS tile layout (36 KB per buffer, two buffers): KV row k (0..31) of the
+// One workgroup = 8 waves = 128 query rows (16 per wave, two waves per SIMD) of
+// one sequence x one split of that sequence's KV positions; one workgroup per
+// CU (its LDS ring).
+//
+// LDS: a ring of 4 KV tiles of 32 rows (36 KB each). KV row k (0..31) of a
 // tile, 16-byte chunk c (0..71) of that row lives at
 //   (c / 8) * 4096 + k * 128 + ((c % 8) ^ swz(k)) * 16.
-// Wave w loads KV rows 8w..8w+7 of each tile: 9 direct-to-LDS loads of 1 KB
-// (one per chunk group), lane -> (row 8w + lane/8, chunk position lane%8).
+// Waves 0..3 gather the tiles: wave w loads KV rows 8w..8w+7 with 9
+// direct-to-LDS loads of 1 KB (one per chunk group), lane -> (row 8w + lane/8,
+// chunk position lane%8). The slot-table entries of those 8 rows are read with
+// scalar loads one tile ahead. Tiles it+1..it+3 are in flight while tile it is
+// used; one barrier per tile both publishes tile it and frees the buffer the
+// next load writes (the one tile it-1 used). Past the end of the split the
+// loads repeat the split's last row, so every loading wave always has exactly
+// 3 tiles (27 loads) outstanding and waits with a constant count.
 //
-// Per wave, per tile (16 query rows, 32 keys):
-//   S^T[32 keys x 16 rows] = K[32 x 576] . Q^T   : 2 key blocks x 18 MFMA 16x16x32
-//   lane l holds keys {4g+i, 16+4g+i} (g = l/16, i < 4) of query row l%16
-//   P^T (bf16) is then exactly the B operand of O^T += V^T P^T (k = 32 keys),
-//   and V^T is read with ds_read_tr16_b64 from the same K-major tile.
-//   O^T lane l holds features {16cb + 4g + i} of query row l%16.
-__global__ __launch_bounds__(NW * 64, 2) void verify_attn_partial_kernel(PartialArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_BYTES];
+// Per wave, per tile (16 query rows r, 32 keys j), MFMA 16x16x32 bf16:
+//   S^T[j, r] = K[j, :] . Q[r, :]      2 key blocks x 18 k-steps; A = K from LDS,
+//     B = Q^T in VGPRs; lane l then holds row r = l%16, keys {4g+i, 16+4g+i}
+//     (g = l/16, i < 4)
+//   O^T[n, r] += V^T[n, j] P^T[j, r]   per 16-feature block, one k-step of 32
+//     keys; B = P^T is the bf16 score fragment itself (no lane exchange), A =
+//     V^T comes from the K-major tile with the LDS transpose read.
+//     O^T lane l holds row r = l%16, features 16cb + 4g + i.
+// Operand reads run a few MFMAs ahead of use; scheduling barriers stop the
+// compiler from hoisting more of them than the register budget allows.
+__global__ __launch_bounds__(NWAVES * 64, 1) void verify_attn_partial_kernel(PartialArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * TILE_BYTES];
   __shared__ unsigned long long anc_s[MAX_TREE];
 
   const int lane = threadIdx.x & 63;
@@ -273,46 +314,62 @@ __global__ __launch_bounds__(NW * 64, 2) void verify_attn_partial_kernel(Partial
   }
 
   // Query fragments (B operand of S^T = K Q^T): 8 features per k-step.
-  const int qrow = rt * ROWS_PER_TILE + wave * ROWS_PER_WAVE + (lane & 15);
+  const int row0 = rt * ROWS_PER_TILE + wave * ROWS_PER_WAVE;
+  const bool wave_active = row0 < a.M;  // wave-uniform: this wave has query rows
+  const int qrow = row0 + (lane & 15);
   const bool row_ok = qrow < a.M;
   const int lg = lane >> 4;  // lane group 0..3
   bf16x8 qf[QK_STEPS];
-  {
-    const uint16_t* src = a.q + ((int64_t)loc.b * a.M + (row_ok ? qrow : 0)) * KV_DIM + 8 * lg;
+  if (wave_active) {
+    const uint16_t* src = a.q + ((int64_t)loc.b * a.M + (row_ok ? qrow : row0)) * KV_DIM + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < QK_STEPS; ++ks) {
       u32x4 v = *reinterpret_cast<const u32x4*>(src + 32 * ks);
       if (!row_ok) v = u32x4{0u, 0u, 0u, 0u};
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
+    wait_vmcnt<0>();  // before any tile load is in flight
   }
 
-  // Loader lane mapping.
-  const int ld_row = wave * ROWS_PER_WAVE_LOAD + (lane >> 3);
+  // ---- KV tile gather (waves 0..LOAD_WAVES-1)
+  const bool loader = wave < LOAD_WAVES;
+  const int ld_row = wave * ROWS_PER_LOAD_WAVE + (lane >> 3);
   const int ld_pos = lane & 7;
   const int ld_elem = 8 * (ld_pos ^ swz(ld_row));
+  const int ld_sel = lane >> 3;
   const int64_t slot_hi = a.total_kv - 1;
-  const int64_t pool_hi = a.pool_slots - 1;
-  // The slot-table value is clamped where it is used, so that the load's
-  // latency overlaps the previous tile's compute.
-  auto load_slot = [&](int key0) -> int {
-    int key = key0 + ld_row;
-    key = key < k1 ? key : k1 - 1;
-    int64_t si = loc.seg + key;
-    si = si < slot_hi ? si : slot_hi;
-    return a.slot_idx[si];
+  const int pool_hi = (int)(a.pool_slots - 1 < (int64_t)INT32_MAX ? a.pool_slots - 1 : (int64_t)INT32_MAX);
+  const __attribute__((address_space(4))) int32_t* slot_tab =
+      (const __attribute__((address_space(4))) int32_t*)(a.slot_idx);
+  // Slot-table entries of this wave's 8 rows of the tile starting at key kt
+  // (wave-uniform scalar loads; keys past the split end repeat its last key).
+  auto tile_slots = [&](int kt, int (&s)[ROWS_PER_LOAD_WAVE]) {
+#pragma unroll
+    for (int r = 0; r < ROWS_PER_LOAD_WAVE; ++r) {
+      int key = kt + wave * ROWS_PER_LOAD_WAVE + r;
+      key = key < k1 ? key : k1 - 1;
+      int64_t si = loc.seg + key;
+      si = si < slot_hi ? si : slot_hi;
+      s[r] = slot_tab[si];
+    }
   };
   const uint32_t smem_base = lds_addr(smem);
-  auto issue_tile = [&](int slot, uint32_t buf) {
-    int64_t s = slot < 0 ? 0 : slot;
-    s = s > pool_hi ? pool_hi : s;
-    const uint16_t* src = a.kv + s * KV_DIM + ld_elem;
-    const uint32_t dst = buf + wave * (ROWS_PER_WAVE_LOAD * 128);
+  auto issue_tile = [&](const int (&s)[ROWS_PER_LOAD_WAVE], int buf) {
+    // Lane picks the entry of its row (lane / 8) with a 3-level select, so the
+    // eight scalar values never go through an indexed (scratch) array.
+    const bool b0 = ld_sel & 1, b1 = ld_sel & 2, b2 = ld_sel & 4;
+    const int s01 = b0 ? s[1] : s[0], s23 = b0 ? s[3] : s[2];
+    const int s45 = b0 ? s[5] : s[4], s67 = b0 ? s[7] : s[6];
+    const int s03 = b1 ? s23 : s01, s47 = b1 ? s67 : s45;
+    int slot = b2 ? s47 : s03;
+    slot = slot < 0 ? 0 : (slot > pool_hi ? pool_hi : slot);
+    const uint16_t* src = a.kv + (int64_t)slot * KV_DIM + ld_elem;
+    const uint32_t dst = smem_base + buf * TILE_BYTES + wave * (ROWS_PER_LOAD_WAVE * 128);
 #pragma unroll
     for (int j = 0; j < CHUNK_GROUPS; ++j) load_to_lds16(src + 64 * j, dst + j * GROUP_BYTES);
   };
 
-  // Operand read offsets inside a tile.
+  // Operand read offsets inside a tile (the chunk group is added as a constant).
   const int ql = lane & 15;
   int qk_off[2][2];  // [k-step parity][key block]
 #pragma unroll
@@ -341,37 +398,47 @@ __global__ __launch_bounds__(NW * 64, 2) void verify_attn_partial_kernel(Partial
   float l_run = 0.f;        // this lane's share of the running sum
 
   const int ntiles = (k1 - k0 + NK - 1) / NK;
-  int slot_next = load_slot(k0);
-  issue_tile(slot_next, smem_base);
-  if (ntiles > 1) slot_next = load_slot(k0 + NK);
-
-  __syncthreads();  // anc_s visible
-  const unsigned long long anc = anc_s[row_ok ? qrow / a.H : 0];
+  int next_slots[ROWS_PER_LOAD_WAVE];
+  if (loader) {
+#pragma unroll
+    for (int t = 0; t < PREFETCH; ++t) {
+      int s0[ROWS_PER_LOAD_WAVE];
+      tile_slots(k0 + t * NK, s0);
+      issue_tile(s0, t);
+    }
+    tile_slots(k0 + PREFETCH * NK, next_slots);
+  }
 
   for (int it = 0; it < ntiles; ++it) {
-    const uint32_t cur = smem_base + (it & 1) * TILE_BYTES;
-    if (it + 1 < ntiles) {
-      issue_tile(slot_next, smem_base + ((it + 1) & 1) * TILE_BYTES);
-      if (it + 2 < ntiles) {
-        slot_next = load_slot(k0 + (it + 2) * NK);
-        wait_vmcnt<CHUNK_GROUPS + 1>();
-      } else {
-        wait_vmcnt<CHUNK_GROUPS>();
-      }
-    } else {
-      wait_vmcnt<0>();
+    if (loader) wait_vmcnt<(PREFETCH - 1) * CHUNK_GROUPS>();  // this wave's part of tile `it` landed
+    lds_barrier();  // tile `it` complete; every wave is done with tile it-1's buffer
+    if (loader) {
+      issue_tile(next_slots, (it + PREFETCH) % NBUF);
+      tile_slots(k0 + (it + PREFETCH + 1) * NK, next_slots);
     }
-    lds_barrier();
+    if (!wave_active) continue;
+    const uint32_t cur = smem_base + (it % NBUF) * TILE_BYTES;
 
-    // ---- S^T = K Q^T
+    // ---- S^T = K Q^T: 36 MFMAs, k-step s = 2 ks + key block
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    {
+      auto kread = [&](int st) {
+        const int ks = st >> 1, kb = st & 1;
+        return lds_read_b128(cur + (ks >> 1) * GROUP_BYTES + qk_off[ks & 1][kb]);
+      };
+      bf16x8 kbuf[QK_AHEAD];
 #pragma unroll
-    for (int ks = 0; ks < QK_STEPS; ++ks) {
-      const uint32_t base = cur + (ks >> 1) * GROUP_BYTES;
-      const bf16x8 k0v = lds_read_b128(base + qk_off[ks & 1][0]);
-      const bf16x8 k1v = lds_read_b128(base + qk_off[ks & 1][1]);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0v, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1v, qf[ks], s1, 0, 0, 0);
+      for (int st = 0; st < QK_AHEAD; ++st) kbuf[st] = kread(st);
+#pragma unroll
+      for (int st = 0; st < 2 * QK_STEPS; ++st) {
+        const bf16x8 kv = kbuf[st % QK_AHEAD];
+        if (st + QK_AHEAD < 2 * QK_STEPS) kbuf[st % QK_AHEAD] = kread(st + QK_AHEAD);
+        if (st & 1)
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qf[st >> 1], s1, 0, 0, 0);
+        else
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qf[st >> 1], s0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
     // ---- scale, tree mask, online softmax (base 2)
@@ -383,6 +450,7 @@ __global__ __launch_bounds__(NW * 64, 2) void verify_attn_partial_kernel(Partial
     }
     const int kt = k0 + it * NK;
     if (kt + NK > k1 || kt + NK > P) {
+      const unsigned long long anc = anc_s[row_ok ? qrow / a.H : 0];
       const int kb0 = kt + 4 * lg;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -394,11 +462,11 @@ __global__ __launch_bounds__(NW * 64, 2) void verify_attn_partial_kernel(Partial
     }
     float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, xor16(mx));
+    mx = fmaxf(mx, xor32(mx));
     const bool raise = mx > m_run + LAZY_RESCALE_LOG2;
     if (__ballot(raise)) {
-      const float alpha = raise ? exp2f(m_run - mx) : 1.0f;  // m_run = -inf -> 0
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;  // m_run = -inf -> 0
       m_run = raise ? mx : m_run;
       l_run *= alpha;
 #pragma unroll
@@ -407,7 +475,7 @@ __global__ __launch_bounds__(NW * 64, 2) void verify_attn_partial_kernel(Partial
     const float mu = (m_run == -INFINITY) ? 0.f : m_run;
     float p[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = exp2f(sv[e] - mu);
+    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e] - mu);
     const bf16x8 pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
                        (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
     {
@@ -420,21 +488,32 @@ __global__ __launch_bounds__(NW * 64, 2) void verify_attn_partial_kernel(Partial
       l_run += acc;
     }
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T: 32 MFMAs, one per 16-feature block
+    {
+      auto vread = [&](int cb) {
+        const uint32_t base = cur + (cb >> 2) * GROUP_BYTES;
+        const bf16x4 v0 = lds_read_tr(base + pv_off[cb & 3][0]);
+        const bf16x4 v1 = lds_read_tr(base + pv_off[cb & 3][1]);
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 vbuf[PV_AHEAD];
 #pragma unroll
-    for (int cb = 0; cb < PV_BLOCKS; ++cb) {
-      const uint32_t base = cur + (cb >> 2) * GROUP_BYTES;
-      const bf16x4 v0 = lds_read_tr(base + pv_off[cb & 3][0]);
-      const bf16x4 v1 = lds_read_tr(base + pv_off[cb & 3][1]);
-      const bf16x8 vt = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, o[cb], 0, 0, 0);
+      for (int cb = 0; cb < PV_AHEAD; ++cb) vbuf[cb] = vread(cb);
+#pragma unroll
+      for (int cb = 0; cb < PV_BLOCKS; ++cb) {
+        const bf16x8 vt = vbuf[cb % PV_AHEAD];
+        if (cb + PV_AHEAD < PV_BLOCKS) vbuf[cb % PV_AHEAD] = vread(cb + PV_AHEAD);
+        o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, o[cb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    lds_barrier();  // every wave is done with `cur` before it is refilled
   }
+  if (loader) wait_vmcnt<0>();  // no tile load outlives the workgroup
 
+  if (!wave_active) return;
   // ---- partial results of this split
-  float l_row = l_run + __shfl_xor(l_run, 16);
-  l_row += __shfl_xor(l_row, 32);
+  float l_row = l_run + xor16(l_run);
+  l_row += xor32(l_row);
   if (row_ok) {
     const int64_t rowid = (int64_t)g * a.M + qrow;
     float* po = a.part_o + rowid * V_DIM + 4 * lg;
@@ -448,36 +527,72 @@ __global__ __launch_bounds__(NW * 64, 2) void verify_attn_partial_kernel(Partial
 }
 
 // ------------------------------------------------------------ combine kernel
-// One wave per output row (b, r); lane covers 8 consecutive features.
-// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s, in
-// split order, rounded to bf16 (nearest even).
-__global__ __launch_bounds__(COMBINE_ROWS_PER_BLOCK * 64) void verify_attn_combine_kernel(CombineArgs a) {
+// Output row (b, r) = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
+// sequence's splits s, M = max_s m_s, rounded to bf16 (nearest even).
+// WPR waves share one row: wave k reduces splits k, k + WPR, ... in order, and
+// the WPR wave results are merged in wave order through LDS, so the result
+// does not depend on timing. Lane j covers features 8j .. 8j+7.
+template <int WPR>
+__global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_kernel(CombineArgs a) {
+  constexpr int WAVES = WPR < 4 ? 4 : WPR;
+  constexpr int ROWS = WAVES / WPR;
+  __shared__ float red_ml[WAVES][2];
+  __shared__ f32x4 red_o[WPR > 1 ? WAVES : 1][2 * 64];
+
   const int lane = threadIdx.x & 63;
-  const int64_t grow = (int64_t)blockIdx.x * COMBINE_ROWS_PER_BLOCK + (threadIdx.x >> 6);
-  if (grow >= (int64_t)a.B * a.M) return;
-  const int b = (int)(grow / a.M);
-  const int row = (int)(grow - (int64_t)b * a.M);
+  const int wave = threadIdx.x >> 6;
+  const int sub = wave % WPR;
+  const int64_t grow = (int64_t)blockIdx.x * ROWS + wave / WPR;
+  const bool active = grow < (int64_t)a.B * a.M;
+  const int b = active ? (int)(grow / a.M) : 0;
+  const int row = active ? (int)(grow - (int64_t)b * a.M) : 0;
 
   SplitLoc loc;
-  if (!locate_split(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, b, true, &loc)) return;
+  loc.g0 = 0;
+  loc.n_splits = 0;
+  if (active && !locate_split(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, b, true, &loc)) loc.n_splits = 0;
   int g_end = loc.g0 + loc.n_splits;
   g_end = g_end < a.max_splits ? g_end : a.max_splits;
 
-  float mmax = -INFINITY;
-  for (int g = loc.g0; g < g_end; ++g) mmax = fmaxf(mmax, a.part_ml[2 * ((int64_t)g * a.M + row)]);
+  float mloc = -INFINITY;
+  for (int g = loc.g0 + sub; g < g_end; g += WPR) mloc = fmaxf(mloc, a.part_ml[2 * ((int64_t)g * a.M + row)]);
 
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  for (int g = loc.g0; g < g_end; ++g) {
+  for (int g = loc.g0 + sub; g < g_end; g += WPR) {
     const int64_t rowid = (int64_t)g * a.M + row;
     const float m = a.part_ml[2 * rowid];
     const float l = a.part_ml[2 * rowid + 1];
-    const float w = (m == -INFINITY) ? 0.f : exp2f(m - mmax);
+    const float w = (m == -INFINITY) ? 0.f : exp2f(m - mloc);
     const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + rowid * V_DIM + 8 * lane);
     acc0 += w * src[0];
     acc1 += w * src[1];
     L += w * l;
   }
+
+  if constexpr (WPR > 1) {
+    if (lane == 0) {
+      red_ml[wave][0] = mloc;
+      red_ml[wave][1] = L;
+    }
+    red_o[wave][2 * lane] = acc0;
+    red_o[wave][2 * lane + 1] = acc1;
+    __syncthreads();
+    if (sub != 0) return;
+    float mm = -INFINITY;
+    for (int k = 0; k < WPR; ++k) mm = fmaxf(mm, red_ml[wave + k][0]);
+    acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    L = 0.f;
+    for (int k = 0; k < WPR; ++k) {
+      const float mk = red_ml[wave + k][0];
+      const float w = (mk == -INFINITY) ? 0.f : exp2f(mk - mm);
+      acc0 += w * red_o[wave + k][2 * lane];
+      acc1 += w * red_o[wave + k][2 * lane + 1];
+      L += w * red_ml[wave + k][1];
+    }
+  }
+  if (!active) return;
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   u32x4 packed;
   packed[0] = (uint32_t)f32_to_bf16_rne(acc0[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc0[1] * inv) << 16);
@@ -489,7 +604,7 @@ __global__ __launch_bounds__(COMBINE_ROWS_PER_BLOCK * 64) void verify_attn_combi
 
 // ------------------------------------------------------------------- host
 
-constexpr int TARGET_BLOCKS = 512;  // partial workgroups the automatic split aims for
+constexpr int NUM_CUS = 256;        // MI355X compute units (one partial workgroup each)
 constexpr int MIN_CHUNK = 256;      // keys per split below which partials dominate
 
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -517,21 +632,39 @@ int make_plan(const verify_attn_params* p, Plan* pl) {
   if (p->nsplit > 0) {
     chunk = ceil_div64(p->max_seq_len, p->nsplit);
   } else {
-    chunk = ceil_div64(p->total_kv * row_tiles, TARGET_BLOCKS);
-    if (chunk < MIN_CHUNK) chunk = MIN_CHUNK;
+    // Fewest full rounds of one workgroup per CU: try 1, 2 and 4 workgroups per
+    // CU and keep the split length with the smallest (rounds x keys per split).
+    int64_t best = 0, best_cost = INT64_MAX;
+    for (int64_t per_cu = 1; per_cu <= 4; per_cu *= 2) {
+      int64_t c = ceil_div64(p->total_kv * row_tiles, NUM_CUS * per_cu);
+      c = ceil_div64(c < MIN_CHUNK ? MIN_CHUNK : c, NK) * NK;
+      const int64_t items = (ceil_div64(p->total_kv, c) + p->num_seqs - 1) * row_tiles;
+      const int64_t cost = ceil_div64(items, NUM_CUS) * c;
+      if (cost < best_cost) {
+        best_cost = cost;
+        best = c;
+      }
+    }
+    chunk = best;
   }
   chunk = ceil_div64(chunk, NK) * NK;
   const int64_t len_cap = ceil_div64(p->max_seq_len, NK) * NK;
   if (chunk > len_cap) chunk = len_cap;
   const int64_t max_splits = ceil_div64(p->total_kv, chunk) + p->num_seqs;
   const int64_t blocks = ceil_div64(max_splits * row_tiles, 8) * 8;
-  const int64_t cblocks = ceil_div64((int64_t)p->num_seqs * M, COMBINE_ROWS_PER_BLOCK);
+  // Combine: enough waves per row that the split partials are read with many
+  // loads in flight even when there are few rows.
+  const int64_t rows = (int64_t)p->num_seqs * M;
+  const int64_t seq_splits = ceil_div64(p->max_seq_len, chunk);
+  const int wpr = (seq_splits >= 16 && rows <= 2048) ? 16 : (seq_splits >= 4 ? 4 : 1);
+  const int64_t cblocks = wpr == 1 ? ceil_div64(rows, 4) : rows;
   if (blocks > INT32_MAX || cblocks > INT32_MAX || max_splits > INT32_MAX) return VERIFY_ATTN_ERR_BAD_DIM;
   pl->M = (int)M;
   pl->row_tiles = (int)row_tiles;
   pl->chunk = (int)chunk;
   pl->max_splits = (int)max_splits;
   pl->partial_blocks = (int)blocks;
+  pl->combine_wpr = wpr;
   pl->combine_blocks = (int)cblocks;
   pl->part_o_bytes = (size_t)max_splits * (size_t)M * V_DIM * sizeof(float);
   pl->ws_bytes = pl->part_o_bytes + (size_t)max_splits * (size_t)M * 2 * sizeof(float);
@@ -579,7 +712,7 @@ int launch_partial(const verify_attn_params* p, const Plan& pl, const void* q, c
   a.total_kv = p->total_kv;
   a.pool_slots = p->pool_slots;
   a.qk_scale_log2 = p->sm_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(verify_attn_partial_kernel, dim3(pl.partial_blocks), dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL(verify_attn_partial_kernel, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
   return hipGetLastError() == hipSuccess ? VERIFY_ATTN_OK : VERIFY_ATTN_ERR_LAUNCH_FAILED;
 }
 
@@ -596,8 +729,12 @@ int launch_combine(const verify_attn_params* p, const Plan& pl, const int32_t* s
   a.chunk = pl.chunk;
   a.max_splits = pl.max_splits;
   a.max_seq_len = p->max_seq_len;
-  hipLaunchKernelGGL(verify_attn_combine_kernel, dim3(pl.combine_blocks), dim3(COMBINE_ROWS_PER_BLOCK * 64),
-                     0, stream, a);
+  if (pl.combine_wpr == 16)
+    hipLaunchKernelGGL(verify_attn_combine_kernel<16>, dim3(pl.combine_blocks), dim3(16 * 64), 0, stream, a);
+  else if (pl.combine_wpr == 4)
+    hipLaunchKernelGGL(verify_attn_combine_kernel<4>, dim3(pl.combine_blocks), dim3(4 * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(verify_attn_combine_kernel<1>, dim3(pl.combine_blocks), dim3(4 * 64), 0, stream, a);
   return hipGetLastError() == hipSuccess ? VERIFY_ATTN_OK : VERIFY_ATTN_ERR_LAUNCH_FAILED;
 }
 
@@ -644,7 +781,7 @@ int verify_attn_plan(const verify_attn_params* p, verify_attn_plan_info* info) {
   info->max_splits = pl.max_splits;
   info->partial_blocks = pl.partial_blocks;
   info->combine_blocks = pl.combine_blocks;
-  info->threads_per_block = NW * 64;
+  info->threads_per_block = NWAVES * 64;
   info->reserved = 0;
   return VERIFY_ATTN_OK;
 }
