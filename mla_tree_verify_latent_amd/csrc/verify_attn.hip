@@ -154,6 +154,22 @@ __device__ bool locate_split(const int32_t* __restrict__ seq_lens, int B, int T,
   return false;
 }
 
+// Total number of splits over all sequences (same clamping as locate_split),
+// computed by one wave; every wave of a workgroup gets the same answer.
+__device__ int count_splits(const int32_t* __restrict__ seq_lens, int B, int T, int max_len, int chunk) {
+  const int lane = threadIdx.x & 63;
+  int total = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    int ns = 0;
+    if (b < B) ns = (clamp_len(seq_lens[b], T, max_len) + chunk - 1) / chunk;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) ns += __shfl_xor(ns, d);
+    total += ns;
+  }
+  return total;
+}
+
 // Swizzle of the 16-byte chunk position inside a 128-byte row segment. The LDS
 // serves 256 bytes per clock (64 banks x 4 bytes = 16 chunk slots); a chunk at
 // byte address A sits in slot (A / 16) % 16 = 8 * (row & 1) + position, with
@@ -278,14 +294,19 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void verify_attn_partial_kernel(Par
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // XCD-aware order: consecutive workgroup ids go to different XCDs, so hand
-  // each XCD a contiguous range of (split, row tile) pairs; the row tiles of
-  // one split then share that XCD's L2 for their KV reads.
-  const int per_xcd = gridDim.x >> 3;
-  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  // XCD-aware order: workgroup ids are dealt to the 8 XCDs round-robin, so give
+  // each XCD a contiguous, equal share of the (split, row tile) work items that
+  // exist for these sequence lengths; the row tiles of one split then share that
+  // XCD's L2 for their KV reads, and no XCD gets more items than another.
+  int n_items = count_splits(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk);
+  n_items = __builtin_amdgcn_readfirstlane(min(n_items, a.max_splits) * a.row_tiles);
+  const int per_xcd = (n_items + 7) >> 3;
+  const int k_on_xcd = blockIdx.x >> 3;
+  if (k_on_xcd >= per_xcd) return;
+  const int logical = (blockIdx.x & 7) * per_xcd + k_on_xcd;
+  if (logical >= n_items) return;
   const int g = logical / a.row_tiles;
   const int rt = logical - g * a.row_tiles;
-  if (g >= a.max_splits) return;
 
   SplitLoc loc;
   if (!locate_split(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, g, false, &loc)) return;
@@ -319,6 +340,19 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void verify_attn_partial_kernel(Par
   const int qrow = row0 + (lane & 15);
   const bool row_ok = qrow < a.M;
   const int lg = lane >> 4;  // lane group 0..3
+  // Touch the split's slot-table lines (one 4-byte load per 128-byte line) so
+  // the per-tile scalar loads of the entries hit L2; the loads complete with
+  // the query loads below.
+  {
+    int warm = 0;
+    const int nlines = (k1 - k0 + 31) >> 5;
+    for (int i = threadIdx.x; i < nlines; i += NWAVES * 64) {
+      int64_t si = loc.seg + k0 + 32 * (int64_t)i;
+      si = si < a.total_kv - 1 ? si : a.total_kv - 1;
+      warm ^= a.slot_idx[si];
+    }
+    asm volatile("" ::"v"(warm));
+  }
   bf16x8 qf[QK_STEPS];
   if (wave_active) {
     const uint16_t* src = a.q + ((int64_t)loc.b * a.M + (row_ok ? qrow : row0)) * KV_DIM + 8 * lg;
@@ -328,8 +362,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void verify_attn_partial_kernel(Par
       if (!row_ok) v = u32x4{0u, 0u, 0u, 0u};
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
-    wait_vmcnt<0>();  // before any tile load is in flight
   }
+  wait_vmcnt<0>();  // query and slot-table loads done before any tile load is in flight
 
   // ---- KV tile gather (waves 0..LOAD_WAVES-1)
   const bool loader = wave < LOAD_WAVES;
