@@ -194,6 +194,51 @@ def traffic_from_counters(partial_ms):
     return c["hbm_bytes_per_launch"]
 
 
+def _read_counter_csv(path, kernel_substr):
+    import csv
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        if kernel_substr in r["Kernel_Name"]:
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+
+def summarize(args):
+    """Write committed summaries from rocprofv3 CSV output (see --summarize)."""
+    out = {}
+    if args.kernel_stats:
+        import csv
+        rows = list(csv.DictReader(open(args.kernel_stats)))
+        lines = ["| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+        for r in rows:
+            lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+                         f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | {float(r['Percentage']):.1f}% |")
+        print("\n".join(lines))
+        return
+    # FETCH_SIZE / WRITE_SIZE of the partial kernel, scaled by a 1 GiB copy's counters.
+    fetch, nf = _read_counter_csv(args.fetch, "verify_attn_partial")
+    write, nw = _read_counter_csv(args.write, "verify_attn_partial")
+    cfetch, _ = _read_counter_csv(args.copy_fetch, "copyBuffer")
+    cwrite, _ = _read_counter_csv(args.copy_write, "copyBuffer")
+    copy_bytes = float(1 << 30)
+    f_scale = copy_bytes / (cfetch["FETCH_SIZE"] * 1024)
+    w_scale = copy_bytes / (cwrite["WRITE_SIZE"] * 1024)
+    fb = fetch["FETCH_SIZE"] * 1024 * f_scale
+    wb = write["WRITE_SIZE"] * 1024 * w_scale
+    out = {
+        "kernel": "verify_attn_partial_kernel", "workload": "c4a_long_scattered",
+        "kernel_source_sha256_16": kernel_source_digest(),
+        "fetch_kib_per_dispatch": fetch["FETCH_SIZE"], "write_kib_per_dispatch": write["WRITE_SIZE"],
+        "dispatches": [nf.get("FETCH_SIZE"), nw.get("WRITE_SIZE")],
+        "copy_calibration": {"bytes_read_and_written": copy_bytes,
+                             "fetch_kib": cfetch["FETCH_SIZE"], "write_kib": cwrite["WRITE_SIZE"],
+                             "fetch_scale": f_scale, "write_scale": w_scale},
+        "hbm_read_bytes_per_launch": fb, "hbm_write_bytes_per_launch": wb,
+        "hbm_bytes_per_launch": fb + wb,
+    }
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,7 +251,18 @@ def main():
     ap.add_argument("--stage", default=None, choices=[None, "full", "partial", "combine", "copy"],
                     help="profiling aid: only run K calls of one stage of the headline workload; "
                          "'copy' runs K device-to-device copies of 1 GiB (counter calibration)")
+    ap.add_argument("--summarize", action="store_true",
+                    help="no GPU: print a summary of rocprofv3 CSV output (--kernel-stats, or "
+                         "--fetch/--write/--copy-fetch/--copy-write counter files)")
+    ap.add_argument("--kernel-stats")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the verify path has no multi-GPU mode "

@@ -19,8 +19,8 @@
  *              or an ancestor of t
  *   out[b,t,h,:] = softmax_j(sm_scale * q[b,t,h,:] . K_j) weighted sum of V_j
  *
- * The library is "paged + bf16 + segmented" behind a C ABI ("The Checkpoint
- * Report", Architecture of the Report) and capture-safe: it consumes the
+ * The library is the paged, bf16, multi-sequence variant behind a C ABI
+ * ("The Checkpoint Report", Architecture of the Report) and capture-safe: it consumes the
  * caller's buffers, takes a caller-allocated workspace, makes no host
  * synchronisation and no device allocation inside the call ("The Commit That
  * Locked In 6x Decode", 1. Capture-Safe Design), so a call can be recorded in a

@@ -7,8 +7,8 @@
  *
  * What it computes (plain definition, fp64 arithmetic throughout):
  * speculative-decoding verify attention for Multi-head Latent Attention.
- * Draft tokens are verified "against the full KV cache" ("The Milestone
- * Commit", Input Knowledge), in the extend layout where a sequence's prefix
+ * Draft tokens are verified by attending to the whole KV cache ("The
+ * Milestone Commit", Input Knowledge), in the extend layout where a sequence's prefix
  * KV slots come first and the draft tokens' slots follow them, with a custom
  * mask of stride prefix + q_len ("The Checkpoint Report", Mistakes and
  * Incorrect Assumptions). The draft tokens form a DDTree draft tree, so the
