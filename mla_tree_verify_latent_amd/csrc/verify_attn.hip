@@ -170,17 +170,15 @@ __device__ int count_splits(const int32_t* __restrict__ seq_lens, int B, int T, 
   return total;
 }
 
-// Swizzle of the 16-byte chunk position inside a 128-byte row segment. The LDS
-// serves 256 bytes per clock (64 banks x 4 bytes = 16 chunk slots); a chunk at
-// byte address A sits in slot (A / 16) % 16 = 8 * (row & 1) + position, with
-// position = (c % 8) ^ swz(row). Both access patterns of the kernel are then
-// conflict-free:
-//  - MFMA operand reads (ds_read_b128; 16 lanes = 16 consecutive KV rows, one
-//    chunk): over the 8 rows of one parity swz is a bijection of 0..7;
-//  - transpose reads (ds_read_b64_tr_b16; 32 lanes = 4 consecutive rows from a
-//    multiple of 4, times 4 consecutive chunks from a multiple of 4): the two
-//    rows of one parity differ in bit 2 of swz, so their chunk sets never meet.
-__device__ __forceinline__ int swz(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
+// Swizzle of the 16-byte chunk position inside a 128-byte row segment:
+// position = (c % 8) ^ (row % 8). With it both operand access patterns of the
+// kernel run without LDS bank conflicts (measured on gfx950 with the
+// SQ_LDS_BANK_CONFLICT counter): the ds_read_b128 reads of 16 consecutive KV
+// rows at one chunk, and the ds_read_b64_tr_b16 reads of 4 rows x 2 chunks per
+// 16-lane group. (A swizzle that keeps 16 consecutive rows on 16 distinct
+// 16-byte slots of 256 bytes still conflicts: the 128-bit reads are served 8
+// lanes at a time, so 8 consecutive rows must cover all 8 positions.)
+__device__ __forceinline__ int swz(int row) { return row & 7; }
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt in
 // 6:4, lgkmcnt in 11:8. A field at its maximum does not wait.
