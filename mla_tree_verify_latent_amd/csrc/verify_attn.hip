@@ -49,7 +49,8 @@ constexpr int CHUNK_GROUPS = KV_DIM / 64;  // 9 groups of 64 bf16 (8 x 16 B) per
 constexpr int GROUP_BYTES = NK * 128;      // one group for all NK rows: 4 KB
 constexpr int TILE_BYTES = CHUNK_GROUPS * GROUP_BYTES;  // 36 KB
 constexpr int NBUF = 4;                    // LDS ring of KV tiles (144 KB)
-constexpr int PREFETCH = NBUF - 1;         // tiles in flight beyond the one in use
+constexpr int PREFETCH = NBUF - 2;         // tiles in flight beyond the one in use (one
+                                           // buffer stays with the lagging waves' PV)
 constexpr int QK_STEPS = KV_DIM / 32;      // 18 MFMA k-steps of 32 features
 constexpr int PV_BLOCKS = V_DIM / 16;      // 32 output blocks of 16 features
 constexpr float LAZY_RESCALE_LOG2 = 8.0f;  // running max is raised only past +8 (base 2)
@@ -269,11 +270,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // Waves 0..3 gather the tiles: wave w loads KV rows 8w..8w+7 with 9
 // direct-to-LDS loads of 1 KB (one per chunk group), lane -> (row 8w + lane/8,
 // chunk position lane%8). The slot-table entries of those 8 rows are read with
-// scalar loads one tile ahead. Tiles it+1..it+3 are in flight while tile it is
-// used; one barrier per tile both publishes tile it and frees the buffer the
-// next load writes (the one tile it-1 used). Past the end of the split the
-// loads repeat the split's last row, so every loading wave always has exactly
-// 3 tiles (27 loads) outstanding and waits with a constant count.
+// scalar loads one tile ahead. Tiles it+1 and it+2 are in flight while tile it
+// is used and tile it-1 is still read by the lagging waves (below); one barrier
+// per tile both publishes tile it and frees the buffer the next load writes
+// (tile it-2's). Past the end of the split the loads repeat the split's last
+// row, so every loading wave always has exactly 2 tiles (18 loads) outstanding
+// and waits with a constant count.
 //
 // Per wave, per tile (16 query rows r, 32 keys j), MFMA 16x16x32 bf16:
 //   S^T[j, r] = K[j, :] . Q[r, :]      2 key blocks x 18 k-steps; A = K from LDS,
@@ -441,15 +443,46 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void verify_attn_partial_kernel(Par
     tile_slots(k0 + PREFETCH * NK, next_slots);
   }
 
+  // O^T += V^T P^T for the tile in LDS buffer `buf`: 32 MFMAs, one per
+  // 16-feature block.
+  auto pv_tile = [&](uint32_t buf, const bf16x8& pb) {
+    auto vread = [&](int cb) {
+      const uint32_t base = buf + (cb >> 2) * GROUP_BYTES;
+      const bf16x4 v0 = lds_read_tr(base + pv_off[cb & 3][0]);
+      const bf16x4 v1 = lds_read_tr(base + pv_off[cb & 3][1]);
+      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 vbuf[PV_AHEAD];
+#pragma unroll
+    for (int cb = 0; cb < PV_AHEAD; ++cb) vbuf[cb] = vread(cb);
+#pragma unroll
+    for (int cb = 0; cb < PV_BLOCKS; ++cb) {
+      const bf16x8 vt = vbuf[cb % PV_AHEAD];
+      if (cb + PV_AHEAD < PV_BLOCKS) vbuf[cb % PV_AHEAD] = vread(cb + PV_AHEAD);
+      o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, o[cb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Waves 4..7 run half a tile behind waves 0..3 on the same SIMDs: after the
+  // tile barrier they first finish the PV of the previous tile, then QK and the
+  // softmax of this one. One wave's softmax (VALU) then overlaps the other
+  // wave's MFMAs instead of both idling the matrix unit at the same time.
+  // Rescaling O at tile t (a raised running max) comes after PV(t-1) was
+  // added, as the online softmax requires.
+  const bool lagging = wave >= 4;
+  bf16x8 pb_prev = {};
+  uint32_t buf_prev = 0;
   for (int it = 0; it < ntiles; ++it) {
     if (loader) wait_vmcnt<(PREFETCH - 1) * CHUNK_GROUPS>();  // this wave's part of tile `it` landed
-    lds_barrier();  // tile `it` complete; every wave is done with tile it-1's buffer
+    lds_barrier();  // tile `it` complete; every wave is done with tile it-2's buffer
     if (loader) {
       issue_tile(next_slots, (it + PREFETCH) % NBUF);
       tile_slots(k0 + (it + PREFETCH + 1) * NK, next_slots);
     }
     if (!wave_active) continue;
     const uint32_t cur = smem_base + (it % NBUF) * TILE_BYTES;
+    if (lagging && it > 0) pv_tile(buf_prev, pb_prev);
 
     // ---- S^T = K Q^T: 36 MFMAs, k-step s = 2 ks + key block
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -520,26 +553,14 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void verify_attn_partial_kernel(Par
       l_run += acc;
     }
 
-    // ---- O^T += V^T P^T: 32 MFMAs, one per 16-feature block
-    {
-      auto vread = [&](int cb) {
-        const uint32_t base = cur + (cb >> 2) * GROUP_BYTES;
-        const bf16x4 v0 = lds_read_tr(base + pv_off[cb & 3][0]);
-        const bf16x4 v1 = lds_read_tr(base + pv_off[cb & 3][1]);
-        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      bf16x8 vbuf[PV_AHEAD];
-#pragma unroll
-      for (int cb = 0; cb < PV_AHEAD; ++cb) vbuf[cb] = vread(cb);
-#pragma unroll
-      for (int cb = 0; cb < PV_BLOCKS; ++cb) {
-        const bf16x8 vt = vbuf[cb % PV_AHEAD];
-        if (cb + PV_AHEAD < PV_BLOCKS) vbuf[cb % PV_AHEAD] = vread(cb + PV_AHEAD);
-        o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, o[cb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    if (lagging) {
+      pb_prev = pb;
+      buf_prev = cur;
+    } else {
+      pv_tile(cur, pb);
     }
   }
+  if (lagging && wave_active) pv_tile(buf_prev, pb_prev);
   if (loader) wait_vmcnt<0>();  // no tile load outlives the workgroup
 
   if (!wave_active) return;
