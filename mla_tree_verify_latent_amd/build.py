@@ -2,8 +2,10 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc", "verify_attn.hip")
@@ -15,8 +17,42 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Werror",
     # keep the compiler from forming packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMAs the compiler emits keep their accumulators in VGPRs: the AGPRs are
+    # reserved for the partial kernel's output accumulators (asm MFMAs)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE,
 ]
+
+
+def check_registers(extra=()) -> dict:
+    """Compile the device code to assembly and check the partial kernel's
+    register allocation: no spills, and exactly the 256 AGPRs of the output
+    accumulators (the asm MFMAs rely on the compiler never touching them)."""
+    with tempfile.TemporaryDirectory() as tmp:
+        asm = os.path.join(tmp, "verify_attn.s")
+        cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC", "-Werror")], *extra,
+               "--cuda-device-only", "-S", SRC, "-o", asm]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc -S failed ({res.returncode}): {' '.join(cmd)}")
+        text = open(asm).read()
+    meta = text[text.index("amdhsa.kernels"):]
+    info = {}
+    for block in meta.split("  - .agpr_count:")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block).group(1)
+        info[name] = {
+            "agpr": int(block.split()[0]),
+            "vgpr_spill": int(re.search(r"\.vgpr_spill_count:\s+(\d+)", block).group(1)),
+            "sgpr_spill": int(re.search(r"\.sgpr_spill_count:\s+(\d+)", block).group(1)),
+        }
+    partial = [v for k, v in info.items() if "partial" in k]
+    if len(partial) != 1:
+        raise RuntimeError(f"partial kernel not found in the assembly metadata: {sorted(info)}")
+    p = partial[0]
+    if p["vgpr_spill"] or p["sgpr_spill"] or p["agpr"] != 256:
+        raise RuntimeError(f"partial kernel register allocation changed: {p}")
+    return info
 
 
 def build(out: str = LIB, extra=()) -> str:
@@ -25,6 +61,7 @@ def build(out: str = LIB, extra=()) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
+    check_registers(extra)
     os.replace(out + ".tmp", out)
     return out
 

@@ -13,14 +13,15 @@
 // ("The Commit That Locked In 6x Decode", 1. Capture-Safe Design).
 //
 // gfx950 design (see the header of verify_attn_partial_kernel for the layout):
-//  - one workgroup = 4 waves = 64 query rows (rows are (node, head) pairs of one
-//    sequence, r = t*H + h) x one split of the sequence's KV positions;
+//  - one workgroup = 4 waves (one per SIMD) = 128 query rows (rows are (node,
+//    head) pairs of one sequence, r = t*H + h) x one split of the sequence's
+//    KV positions; one workgroup per CU;
 //  - KV tiles of 32 rows (36 KB) are gathered straight into LDS with 16-byte
-//    direct-to-LDS loads, one slot-table lookup per row, double-buffered;
-//  - S^T = K Q^T and O^T += V^T P^T on MFMA 16x16x32 bf16, so every lane holds
+//    direct-to-LDS loads, one slot-table lookup per row, three tiles ahead;
+//  - S^T = K Q^T and O^T += V^T P^T on MFMA 32x32x16 bf16, so every lane holds
 //    whole query rows of both the scores and the accumulator (the softmax state
-//    of a row never leaves its lanes); V^T comes from the K-major LDS tile with
-//    the LDS transpose read;
+//    of a row never leaves its lane pair); V^T comes from the K-major LDS tile
+//    with the LDS transpose read; O stays in AGPRs;
 //  - fp32 online softmax in base 2, tree mask from per-node 64-bit ancestor
 //    masks built on the device from the parent pointers;
 //  - a log-sum-exp combine kernel merges the splits and rounds to bf16.
@@ -39,26 +40,26 @@ constexpr int V_DIM = 512;
 constexpr int MAX_TREE = 64;
 
 // Partial kernel geometry.
-constexpr int NWAVES = 8;                  // waves per workgroup (two per SIMD)
-constexpr int ROWS_PER_WAVE = 16;          // query rows per wave (MFMA N for QK and PV)
+constexpr int NWAVES = 4;                  // waves per workgroup (one per SIMD)
+constexpr int ROWS_PER_WAVE = 32;          // query rows per wave (MFMA 32x32 N)
 constexpr int ROWS_PER_TILE = NWAVES * ROWS_PER_WAVE;  // 128 query rows per workgroup
 constexpr int NK = 32;                     // KV rows per LDS tile
-constexpr int LOAD_WAVES = 4;              // waves that gather the KV tiles
-constexpr int ROWS_PER_LOAD_WAVE = NK / LOAD_WAVES;  // 8 KV rows per loading wave
+constexpr int ROWS_PER_LOAD_WAVE = NK / NWAVES;  // 8 KV rows gathered per wave
 constexpr int CHUNK_GROUPS = KV_DIM / 64;  // 9 groups of 64 bf16 (8 x 16 B) per KV row
 constexpr int GROUP_BYTES = NK * 128;      // one group for all NK rows: 4 KB
 constexpr int TILE_BYTES = CHUNK_GROUPS * GROUP_BYTES;  // 36 KB
 constexpr int NBUF = 4;                    // LDS ring of KV tiles (144 KB)
-constexpr int PREFETCH = NBUF - 2;         // tiles in flight beyond the one in use (one
-                                           // buffer stays with the lagging waves' PV)
-constexpr int QK_STEPS = KV_DIM / 32;      // 18 MFMA k-steps of 32 features
-constexpr int PV_BLOCKS = V_DIM / 16;      // 32 output blocks of 16 features
+constexpr int PREFETCH = 3;                // tiles in flight beyond the one in use
+constexpr int SLOT_RING = 4;               // LDS ring of slot-table entries (tiles)
+constexpr int QK_STEPS = KV_DIM / 16;      // 36 MFMA k-steps of 16 features
+constexpr int PV_BLOCKS = V_DIM / 32;      // 16 output blocks of 32 features
 constexpr float LAZY_RESCALE_LOG2 = 8.0f;  // running max is raised only past +8 (base 2)
 constexpr int QK_AHEAD = 4;                // K operand reads in flight ahead of their MFMA
-constexpr int PV_AHEAD = 4;                // V^T operand reads (pairs) in flight ahead
+constexpr int PV_AHEAD = 4;                // V^T operand reads in flight ahead
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -172,14 +173,18 @@ __device__ int count_splits(const int32_t* __restrict__ seq_lens, int B, int T, 
 }
 
 // Swizzle of the 16-byte chunk position inside a 128-byte row segment:
-// position = (c % 8) ^ (row % 8). With it both operand access patterns of the
-// kernel run without LDS bank conflicts (measured on gfx950 with the
-// SQ_LDS_BANK_CONFLICT counter): the ds_read_b128 reads of 16 consecutive KV
-// rows at one chunk, and the ds_read_b64_tr_b16 reads of 4 rows x 2 chunks per
-// 16-lane group. (A swizzle that keeps 16 consecutive rows on 16 distinct
-// 16-byte slots of 256 bytes still conflicts: the 128-bit reads are served 8
-// lanes at a time, so 8 consecutive rows must cover all 8 positions.)
-__device__ __forceinline__ int swz(int row) { return row & 7; }
+// position = (c % 8) ^ swz(row), where swz swaps bits 1 and 2 of row % 8 and
+// flips bit 0 for rows 16..31 of a tile. Both operand access patterns of the
+// kernel then run without LDS bank conflicts (measured on gfx950 with the
+// SQ_LDS_BANK_CONFLICT counter and by read throughput):
+//  - QK, ds_read_b128 (lane l: row l%32, one chunk per lane half): eight
+//    consecutive rows must land on eight distinct positions, and rows r and
+//    r + 16 on positions that differ in bit 0;
+//  - PV, ds_read_b64_tr_b16 (32 lanes: 4 consecutive rows x 4 consecutive
+//    positions from a multiple of 4): rows r and r + 2 must differ in bit 2.
+__device__ __forceinline__ int swz(int row) {
+  return ((row & 1) | (((row >> 2) & 1) << 1) | (((row >> 1) & 1) << 2)) ^ ((row >> 4) & 1);
+}
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt in
 // 6:4, lgkmcnt in 11:8. A field at its maximum does not wait.
@@ -235,17 +240,42 @@ __device__ __forceinline__ void load_to_lds16(const void* gptr, uint32_t lds_bas
       : "v"(gptr), "s"(lds_base)
       : "memory", "m0");
 }
+// 4-byte global -> LDS load: lane l's 4 bytes land at lds_base + 4 * l.
+__device__ __forceinline__ void load_to_lds4(const void* gptr, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(gptr), "s"(lds_base)
+      : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
-// Value of lane l ^ 16 / l ^ 32 (gfx950 permlane swaps; plain VALU, no LDS).
-__device__ __forceinline__ float xor16(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  // r[0]: odd 16-lane rows replaced by the even rows of the source; r[1]: even
-  // rows replaced by the odd rows. Lane l's partner l ^ 16 is in r[1] for even
-  // rows and in r[0] for odd rows.
-  return __builtin_bit_cast(float, ((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
+// acc += A * B with MFMA 32x32x16 bf16 on an accumulator held in AGPRs. The
+// output accumulators of the partial kernel (256 per lane) live in AGPRs for
+// the whole kernel; an asm statement pins them there. The compiler does not
+// model the hazards of an asm MFMA, so the required wait states are explicit:
+// two before it (an operand may have just been written by a VALU instruction)
+// and mfma_drain() before its accumulator is read by anything but another
+// accumulating MFMA.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+__device__ __forceinline__ void mfma_valu_gap() { asm volatile("s_nop 4"); }
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+// acc *= s in place on the AGPRs (bracket with mfma_drain / mfma_valu_gap).
+__device__ __forceinline__ void acc_scale(f32x16& acc, float s) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(acc[i]), "=&v"(tmp)
+                 : "v"(s));
+  }
+}
+
+// Value of lane l ^ 32 (gfx950 permlane swap; plain VALU, no LDS).
 __device__ __forceinline__ float xor32(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
@@ -260,35 +290,38 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 // ------------------------------------------------------------ partial kernel
 //
-// One workgroup = 8 waves = 128 query rows (16 per wave, two waves per SIMD) of
-// one sequence x one split of that sequence's KV positions; one workgroup per
-// CU (its LDS ring).
+// One workgroup = 4 waves (one per SIMD) = 128 query rows (32 per wave) of one
+// sequence x one split of that sequence's KV positions; one workgroup per CU.
 //
 // LDS: a ring of 4 KV tiles of 32 rows (36 KB each). KV row k (0..31) of a
 // tile, 16-byte chunk c (0..71) of that row lives at
 //   (c / 8) * 4096 + k * 128 + ((c % 8) ^ swz(k)) * 16.
-// Waves 0..3 gather the tiles: wave w loads KV rows 8w..8w+7 with 9
+// Every wave gathers 8 rows of each tile: wave w loads KV rows 8w..8w+7 with 9
 // direct-to-LDS loads of 1 KB (one per chunk group), lane -> (row 8w + lane/8,
-// chunk position lane%8). The slot-table entries of those 8 rows are read with
-// scalar loads one tile ahead. Tiles it+1 and it+2 are in flight while tile it
-// is used and tile it-1 is still read by the lagging waves (below); one barrier
-// per tile both publishes tile it and frees the buffer the next load writes
-// (tile it-2's). Past the end of the split the loads repeat the split's last
-// row, so every loading wave always has exactly 2 tiles (18 loads) outstanding
-// and waits with a constant count.
+// chunk position lane%8), spread over its MFMAs. The slot-table entries of
+// those rows travel global -> LDS as well (one 4-byte load per lane into a
+// small ring) two tiles before the gather that uses them. Past the end of the
+// split the loads repeat the split's last row, so each wave issues exactly 10
+// loads per tile and waits with a constant count.
 //
-// Per wave, per tile (16 query rows r, 32 keys j), MFMA 16x16x32 bf16:
-//   S^T[j, r] = K[j, :] . Q[r, :]      2 key blocks x 18 k-steps; A = K from LDS,
-//     B = Q^T in VGPRs; lane l then holds row r = l%16, keys {4g+i, 16+4g+i}
-//     (g = l/16, i < 4)
-//   O^T[n, r] += V^T[n, j] P^T[j, r]   per 16-feature block, one k-step of 32
-//     keys; B = P^T is the bf16 score fragment itself (no lane exchange), A =
-//     V^T comes from the K-major tile with the LDS transpose read.
-//     O^T lane l holds row r = l%16, features 16cb + 4g + i.
-// Operand reads run a few MFMAs ahead of use; scheduling barriers stop the
-// compiler from hoisting more of them than the register budget allows.
-__global__ __launch_bounds__(NWAVES * 64, 1) void verify_attn_partial_kernel(PartialArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * TILE_BYTES];
+// Per wave, per tile (32 query rows r, 32 keys j), MFMA 32x32x16 bf16:
+//   S^T[j, r] = K[j, :] . Q[r, :]      36 k-steps of 16 features; A = K from LDS,
+//     B = Q^T in VGPRs; lane l then holds row r = l%32, keys
+//     8(i/4) + 4(l/32) + i%4, i < 16
+//   O^T[n, r] += V^T[n, j] P^T[j, r]   16 blocks of 32 features x 2 k-steps of
+//     16 keys; B = P^T is the bf16 score fragment itself (no lane exchange),
+//     A = V^T comes from the K-major tile with the LDS transpose read, in the
+//     same key order. O^T (256 accumulators per lane) stays in AGPRs; lane l
+//     holds row r = l%32, features 32cb + 8(i/4) + 4(l/32) + i%4.
+// Each K or V^T operand read from LDS feeds 32 query rows.
+//
+// Per tile: QK (36 MFMAs), the online softmax, PV (32 MFMAs). LDS buffers:
+// tile it in use, tiles it+1..it+3 in flight; one barrier per tile publishes
+// tile it and frees tile it-1's buffer for the gather of tile it+3, whose
+// nine loads ride on the MFMAs (five in QK, four in PV).
+__global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void verify_attn_partial_kernel(PartialArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * TILE_BYTES + SLOT_RING * NWAVES * 256];
   __shared__ unsigned long long anc_s[MAX_TREE];
 
   const int lane = threadIdx.x & 63;
@@ -334,245 +367,230 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void verify_attn_partial_kernel(Par
     anc_s[threadIdx.x] = m;
   }
 
-  // Query fragments (B operand of S^T = K Q^T): 8 features per k-step.
+  // Query fragments (B operand of S^T = K Q^T): lane l holds row l%32,
+  // features 16 ks + 8 (l/32) .. +7 of k-step ks. Waves without query rows
+  // run the same schedule on zeros (they still gather their share of the KV).
   const int row0 = rt * ROWS_PER_TILE + wave * ROWS_PER_WAVE;
-  const bool wave_active = row0 < a.M;  // wave-uniform: this wave has query rows
-  const int qrow = row0 + (lane & 15);
+  const bool wave_active = row0 < a.M;  // wave-uniform
+  const int qrow = row0 + (lane & 31);
   const bool row_ok = qrow < a.M;
-  const int lg = lane >> 4;  // lane group 0..3
-  // Touch the split's slot-table lines (one 4-byte load per 128-byte line) so
-  // the per-tile scalar loads of the entries hit L2; the loads complete with
-  // the query loads below.
-  {
-    int warm = 0;
-    const int nlines = (k1 - k0 + 31) >> 5;
-    for (int i = threadIdx.x; i < nlines; i += NWAVES * 64) {
-      int64_t si = loc.seg + k0 + 32 * (int64_t)i;
-      si = si < a.total_kv - 1 ? si : a.total_kv - 1;
-      warm ^= a.slot_idx[si];
-    }
-    asm volatile("" ::"v"(warm));
-  }
+  const int hl = lane >> 5;  // lane half
   bf16x8 qf[QK_STEPS];
-  if (wave_active) {
-    const uint16_t* src = a.q + ((int64_t)loc.b * a.M + (row_ok ? qrow : row0)) * KV_DIM + 8 * lg;
+  {
+    const uint16_t* src = a.q + ((int64_t)loc.b * a.M + (row_ok ? qrow : 0)) * KV_DIM + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < QK_STEPS; ++ks) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(src + 32 * ks);
-      if (!row_ok) v = u32x4{0u, 0u, 0u, 0u};
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (row_ok) v = *reinterpret_cast<const u32x4*>(src + 16 * ks);
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  wait_vmcnt<0>();  // query and slot-table loads done before any tile load is in flight
 
-  // ---- KV tile gather (waves 0..LOAD_WAVES-1)
-  const bool loader = wave < LOAD_WAVES;
+  // ---- KV gather addressing
   const int ld_row = wave * ROWS_PER_LOAD_WAVE + (lane >> 3);
-  const int ld_pos = lane & 7;
-  const int ld_elem = 8 * (ld_pos ^ swz(ld_row));
-  const int ld_sel = lane >> 3;
+  const int ld_elem = 8 * ((lane & 7) ^ swz(ld_row));
   const int64_t slot_hi = a.total_kv - 1;
   const int pool_hi = (int)(a.pool_slots - 1 < (int64_t)INT32_MAX ? a.pool_slots - 1 : (int64_t)INT32_MAX);
-  const __attribute__((address_space(4))) int32_t* slot_tab =
-      (const __attribute__((address_space(4))) int32_t*)(a.slot_idx);
-  // Slot-table entries of this wave's 8 rows of the tile starting at key kt
-  // (wave-uniform scalar loads; keys past the split end repeat its last key).
-  auto tile_slots = [&](int kt, int (&s)[ROWS_PER_LOAD_WAVE]) {
-#pragma unroll
-    for (int r = 0; r < ROWS_PER_LOAD_WAVE; ++r) {
-      int key = kt + wave * ROWS_PER_LOAD_WAVE + r;
-      key = key < k1 ? key : k1 - 1;
-      int64_t si = loc.seg + key;
-      si = si < slot_hi ? si : slot_hi;
-      s[r] = slot_tab[si];
-    }
-  };
   const uint32_t smem_base = lds_addr(smem);
-  auto issue_tile = [&](const int (&s)[ROWS_PER_LOAD_WAVE], int buf) {
-    // Lane picks the entry of its row (lane / 8) with a 3-level select, so the
-    // eight scalar values never go through an indexed (scratch) array.
-    const bool b0 = ld_sel & 1, b1 = ld_sel & 2, b2 = ld_sel & 4;
-    const int s01 = b0 ? s[1] : s[0], s23 = b0 ? s[3] : s[2];
-    const int s45 = b0 ? s[5] : s[4], s67 = b0 ? s[7] : s[6];
-    const int s03 = b1 ? s23 : s01, s47 = b1 ? s67 : s45;
-    int slot = b2 ? s47 : s03;
+  const uint32_t ring_base = smem_base + NBUF * TILE_BYTES + wave * 256;
+  // Slot-table entry of row r of this wave's 8 rows in the tile at key kt
+  // (keys past the split end repeat its last key).
+  auto slot_ptr = [&](int kt, int r) {
+    int key = kt + wave * ROWS_PER_LOAD_WAVE + r;
+    key = key < k1 ? key : k1 - 1;
+    int64_t si = loc.seg + key;
+    si = si < slot_hi ? si : slot_hi;
+    return a.slot_idx + si;
+  };
+  // Slot entries of tile t -> LDS ring entry t % SLOT_RING (lane l: row l%8).
+  auto issue_slots = [&](int t) {
+    load_to_lds4(slot_ptr(k0 + t * NK, lane & 7), ring_base + (t % SLOT_RING) * (NWAVES * 256));
+  };
+  auto ring_slot = [&](int t) {
+    return *(const LDS_AS int*)(uintptr_t)(ring_base + (t % SLOT_RING) * (NWAVES * 256) + 4 * (lane >> 3));
+  };
+  auto gather_src = [&](int slot) {
     slot = slot < 0 ? 0 : (slot > pool_hi ? pool_hi : slot);
-    const uint16_t* src = a.kv + (int64_t)slot * KV_DIM + ld_elem;
-    const uint32_t dst = smem_base + buf * TILE_BYTES + wave * (ROWS_PER_LOAD_WAVE * 128);
-#pragma unroll
-    for (int j = 0; j < CHUNK_GROUPS; ++j) load_to_lds16(src + 64 * j, dst + j * GROUP_BYTES);
+    return a.kv + (int64_t)slot * KV_DIM + ld_elem;
+  };
+  auto gather_dst = [&](int t) {
+    return smem_base + (t % NBUF) * TILE_BYTES + wave * (ROWS_PER_LOAD_WAVE * 128);
   };
 
   // Operand read offsets inside a tile (the chunk group is added as a constant).
-  const int ql = lane & 15;
-  int qk_off[2][2];  // [k-step parity][key block]
-#pragma unroll
-  for (int par = 0; par < 2; ++par)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kr = 16 * kb + ql;
-      qk_off[par][kb] = kr * 128 + ((((4 * par + lg)) ^ swz(kr)) << 4);
-    }
-  int pv_off[4][2];  // [cb % 4][key half]
+  //  QK k-step ks reads chunk 2 ks + l/32 of key row l%32: group ks/4,
+  //  position 2 (ks%4) + l/32.
+  int qk_off[4];
   {
-    const int r = ql >> 2, c = ql & 3;
+    const int kr = lane & 31;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) qk_off[j] = kr * 128 + (((2 * j + hl) ^ swz(kr)) << 4);
+  }
+  //  PV block cb, key half kh: per 16-lane group q = l/16, lane 4 r + c
+  //  addresses features 32 cb + 16 (q%2) + 4c .. +3 of key row
+  //  16 kh + 8 rd + 4 (q/2) + r (rd = 0, 1 for the two halves of the operand):
+  //  chunk 4 cb + 2 (q%2) + c/2 -> group cb/2, position 4 (cb%2) + 2 (q%2) + c/2.
+  int pv_off[2][2][2];  // [kh][cb % 2][rd]
+  {
+    const int q = lane >> 4, r = (lane & 15) >> 2, c = lane & 3;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int kr = 16 * hf + 4 * lg + r;
-        pv_off[j][hf] = kr * 128 + (((2 * j + (c >> 1)) ^ swz(kr)) << 4) + 8 * (c & 1);
-      }
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int cp = 0; cp < 2; ++cp)
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+          const int row = 16 * kh + 8 * rd + 4 * (q >> 1) + r;
+          const int pos = 4 * cp + 2 * (q & 1) + (c >> 1);
+          pv_off[kh][cp][rd] = row * 128 + ((pos ^ swz(row)) << 4) + 8 * (c & 1);
+        }
   }
 
-  f32x4 o[PV_BLOCKS];
+  f32x16 o[PV_BLOCKS];
 #pragma unroll
-  for (int cb = 0; cb < PV_BLOCKS; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < PV_BLOCKS; ++cb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[cb][i] = 0.f;
   float m_run = -INFINITY;  // running reference max (base-2 scaled scores)
   float l_run = 0.f;        // this lane's share of the running sum
 
+
   const int ntiles = (k1 - k0 + NK - 1) / NK;
-  int next_slots[ROWS_PER_LOAD_WAVE];
-  if (loader) {
+  // Prologue: the slot entries of tiles 0..PREFETCH-1 come straight into
+  // registers; then the steady-state load order (iteration i: slots of tile
+  // i + PREFETCH + 2, gather of tile i + PREFETCH) for i = -PREFETCH .. -1.
+  {
+    int s[PREFETCH];
+#pragma unroll
+    for (int t = 0; t < PREFETCH; ++t) s[t] = *slot_ptr(k0 + t * NK, lane >> 3);
+    wait_vmcnt<0>();  // query, slot and tree loads done before the asm loads start
 #pragma unroll
     for (int t = 0; t < PREFETCH; ++t) {
-      int s0[ROWS_PER_LOAD_WAVE];
-      tile_slots(k0 + t * NK, s0);
-      issue_tile(s0, t);
+      issue_slots(t + 2);
+      const uint16_t* src = gather_src(s[t]);
+      const uint32_t dst = gather_dst(t);
+#pragma unroll
+      for (int j = 0; j < CHUNK_GROUPS; ++j) load_to_lds16(src + 64 * j, dst + j * GROUP_BYTES);
     }
-    tile_slots(k0 + PREFETCH * NK, next_slots);
   }
 
-  // O^T += V^T P^T for the tile in LDS buffer `buf`: 32 MFMAs, one per
-  // 16-feature block.
-  auto pv_tile = [&](uint32_t buf, const bf16x8& pb) {
-    auto vread = [&](int cb) {
-      const uint32_t base = buf + (cb >> 2) * GROUP_BYTES;
-      const bf16x4 v0 = lds_read_tr(base + pv_off[cb & 3][0]);
-      const bf16x4 v1 = lds_read_tr(base + pv_off[cb & 3][1]);
-      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    bf16x8 vbuf[PV_AHEAD];
-#pragma unroll
-    for (int cb = 0; cb < PV_AHEAD; ++cb) vbuf[cb] = vread(cb);
-#pragma unroll
-    for (int cb = 0; cb < PV_BLOCKS; ++cb) {
-      const bf16x8 vt = vbuf[cb % PV_AHEAD];
-      if (cb + PV_AHEAD < PV_BLOCKS) vbuf[cb % PV_AHEAD] = vread(cb + PV_AHEAD);
-      o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, o[cb], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // Waves 4..7 run half a tile behind waves 0..3 on the same SIMDs: after the
-  // tile barrier they first finish the PV of the previous tile, then QK and the
-  // softmax of this one. One wave's softmax (VALU) then overlaps the other
-  // wave's MFMAs instead of both idling the matrix unit at the same time.
-  // Rescaling O at tile t (a raised running max) comes after PV(t-1) was
-  // added, as the online softmax requires.
-  const bool lagging = wave >= 4;
-  bf16x8 pb_prev = {};
-  uint32_t buf_prev = 0;
   for (int it = 0; it < ntiles; ++it) {
-    if (loader) wait_vmcnt<(PREFETCH - 1) * CHUNK_GROUPS>();  // this wave's part of tile `it` landed
-    lds_barrier();  // tile `it` complete; every wave is done with tile it-2's buffer
-    if (loader) {
-      issue_tile(next_slots, (it + PREFETCH) % NBUF);
-      tile_slots(k0 + (it + PREFETCH + 1) * NK, next_slots);
-    }
-    if (!wave_active) continue;
+    // Own loads: tile it (issued PREFETCH iterations ago) and the slot entries
+    // of tile it+PREFETCH (issued just after it) have landed.
+    wait_vmcnt<(PREFETCH - 1) * (CHUNK_GROUPS + 1)>();
+    lds_barrier();  // tile `it` complete; every wave is done with tile it-1's buffer
     const uint32_t cur = smem_base + (it % NBUF) * TILE_BYTES;
-    if (lagging && it > 0) pv_tile(buf_prev, pb_prev);
+    const int t_next = it + PREFETCH;
+    const uint16_t* gsrc = gather_src(ring_slot(t_next));
+    const uint32_t gdst = gather_dst(t_next);
+    issue_slots(t_next + 2);
+    // Gather load j (chunk group j) of tile t_next.
+    auto gather = [&](int j) { load_to_lds16(gsrc + 64 * j, gdst + j * GROUP_BYTES); };
 
-    // ---- S^T = K Q^T: 36 MFMAs, k-step s = 2 ks + key block
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // ---- S^T = K Q^T: 36 MFMAs (gather loads 0..4 ride along)
+    f32x16 sv;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sv[i] = 0.f;
     {
-      auto kread = [&](int st) {
-        const int ks = st >> 1, kb = st & 1;
-        return lds_read_b128(cur + (ks >> 1) * GROUP_BYTES + qk_off[ks & 1][kb]);
-      };
+      auto kread = [&](int ks) { return lds_read_b128(cur + (ks >> 2) * GROUP_BYTES + qk_off[ks & 3]); };
       bf16x8 kbuf[QK_AHEAD];
 #pragma unroll
-      for (int st = 0; st < QK_AHEAD; ++st) kbuf[st] = kread(st);
+      for (int ks = 0; ks < QK_AHEAD; ++ks) kbuf[ks] = kread(ks);
 #pragma unroll
-      for (int st = 0; st < 2 * QK_STEPS; ++st) {
-        const bf16x8 kv = kbuf[st % QK_AHEAD];
-        if (st + QK_AHEAD < 2 * QK_STEPS) kbuf[st % QK_AHEAD] = kread(st + QK_AHEAD);
-        if (st & 1)
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qf[st >> 1], s1, 0, 0, 0);
-        else
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qf[st >> 1], s0, 0, 0, 0);
+      for (int ks = 0; ks < QK_STEPS; ++ks) {
+        const bf16x8 kv = kbuf[ks % QK_AHEAD];
+        if (ks + QK_AHEAD < QK_STEPS) kbuf[ks % QK_AHEAD] = kread(ks + QK_AHEAD);
+        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qf[ks], sv, 0, 0, 0);
+        if ((ks & 7) == 3) gather(ks >> 3);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
     // ---- scale, tree mask, online softmax (base 2)
-    float sv[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = s0[i] * a.qk_scale_log2;
-      sv[4 + i] = s1[i] * a.qk_scale_log2;
-    }
+    for (int i = 0; i < 16; ++i) sv[i] *= a.qk_scale_log2;
     const int kt = k0 + it * NK;
-    if (kt + NK > k1 || kt + NK > P) {
+    if (kt + NK > k1 || kt + NK > P) {  // the tile reaches the split end or the tree
       const unsigned long long anc = anc_s[row_ok ? qrow / a.H : 0];
-      const int kb0 = kt + 4 * lg;
+      const int kb0 = kt + 4 * hl;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = kb0 + (e < 4 ? e : 12 + e);
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb0 + 8 * (i >> 2) + (i & 3);
         const int u = key - P;
         const bool vis = key < k1 && (u < 0 || ((anc >> (u & 63)) & 1ull));
-        sv[e] = vis ? sv[e] : -INFINITY;
+        sv[i] = vis ? sv[i] : -INFINITY;
       }
     }
-    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mx = fmaxf(mx, xor16(mx));
-    mx = fmaxf(mx, xor32(mx));
+    float mx = fmaxf(fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7]))),
+                     fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])), fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+    mx = fmaxf(mx, xor32(mx));  // lanes l and l^32 hold the same query row
     const bool raise = mx > m_run + LAZY_RESCALE_LOG2;
     if (__ballot(raise)) {
       const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;  // m_run = -inf -> 0
       m_run = raise ? mx : m_run;
       l_run *= alpha;
+      mfma_drain();
 #pragma unroll
-      for (int cb = 0; cb < PV_BLOCKS; ++cb) o[cb] *= alpha;
+      for (int cb = 0; cb < PV_BLOCKS; ++cb) acc_scale(o[cb], alpha);
+      mfma_valu_gap();
     }
     const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-    float p[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e] - mu);
-    const bf16x8 pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
-                       (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
+    for (int i = 0; i < 16; ++i) sv[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
+    const bf16x8 pb0 = {(__bf16)sv[0], (__bf16)sv[1], (__bf16)sv[2], (__bf16)sv[3],
+                        (__bf16)sv[4], (__bf16)sv[5], (__bf16)sv[6], (__bf16)sv[7]};
+    const bf16x8 pb1 = {(__bf16)sv[8], (__bf16)sv[9], (__bf16)sv[10], (__bf16)sv[11],
+                        (__bf16)sv[12], (__bf16)sv[13], (__bf16)sv[14], (__bf16)sv[15]};
     {
       // The running sum uses the same bf16-rounded weights that enter O.
-      const u32x4 w = __builtin_bit_cast(u32x4, pb);
+      const u32x4 w0 = __builtin_bit_cast(u32x4, pb0), w1 = __builtin_bit_cast(u32x4, pb1);
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        acc += __builtin_bit_cast(float, w[i] << 16) + __builtin_bit_cast(float, w[i] & 0xffff0000u);
+        acc += (__builtin_bit_cast(float, w0[i] << 16) + __builtin_bit_cast(float, w0[i] & 0xffff0000u)) +
+               (__builtin_bit_cast(float, w1[i] << 16) + __builtin_bit_cast(float, w1[i] & 0xffff0000u));
       l_run += acc;
     }
 
-    if (lagging) {
-      pb_prev = pb;
-      buf_prev = cur;
-    } else {
-      pv_tile(cur, pb);
+    // ---- O^T += V^T P^T: 32 MFMAs (16 feature blocks x 2 key halves; gather
+    // loads 5..8 ride along)
+    {
+      auto vread = [&](int st) {  // step st = 2 cb + kh
+        const int cb = st >> 1, kh = st & 1;
+        const uint32_t base = cur + (cb >> 1) * GROUP_BYTES;
+        const bf16x4 v0 = lds_read_tr(base + pv_off[kh][cb & 1][0]);
+        const bf16x4 v1 = lds_read_tr(base + pv_off[kh][cb & 1][1]);
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 vbuf[PV_AHEAD];
+#pragma unroll
+      for (int st = 0; st < PV_AHEAD; ++st) vbuf[st] = vread(st);
+      mfma_valu_gap();  // pb0 / pb1 were just written by VALU instructions
+#pragma unroll
+      for (int st = 0; st < 2 * PV_BLOCKS; ++st) {
+        const bf16x8 vt = vbuf[st % PV_AHEAD];
+        if (st + PV_AHEAD < 2 * PV_BLOCKS) vbuf[st % PV_AHEAD] = vread(st + PV_AHEAD);
+        mfma_acc(o[st >> 1], vt, (st & 1) ? pb1 : pb0);
+        if ((st & 7) == 5) gather(5 + (st >> 3));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
-  if (lagging && wave_active) pv_tile(buf_prev, pb_prev);
-  if (loader) wait_vmcnt<0>();  // no tile load outlives the workgroup
+  wait_vmcnt<0>();  // no load outlives the workgroup
+  mfma_drain();     // O is read below
 
   if (!wave_active) return;
   // ---- partial results of this split
-  float l_row = l_run + xor16(l_run);
-  l_row += xor32(l_row);
+  const float l_row = l_run + xor32(l_run);
   if (row_ok) {
     const int64_t rowid = (int64_t)g * a.M + qrow;
-    float* po = a.part_o + rowid * V_DIM + 4 * lg;
+    float* po = a.part_o + rowid * V_DIM + 4 * hl;
 #pragma unroll
-    for (int cb = 0; cb < PV_BLOCKS; ++cb) *reinterpret_cast<f32x4*>(po + 16 * cb) = o[cb];
-    if (lg == 0) {
+    for (int cb = 0; cb < PV_BLOCKS; ++cb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<f32x4*>(po + 32 * cb + 8 * i4) =
+            f32x4{o[cb][4 * i4], o[cb][4 * i4 + 1], o[cb][4 * i4 + 2], o[cb][4 * i4 + 3]};
+    if (hl == 0) {
       a.part_ml[2 * rowid] = m_run;
       a.part_ml[2 * rowid + 1] = l_row;
     }
