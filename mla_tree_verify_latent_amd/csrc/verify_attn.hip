@@ -473,33 +473,43 @@ void verify_attn_partial_kernel(PartialArgs a) {
     }
   }
 
+  const uint16_t* gsrc = a.kv;  // gather source / destination of the tile in flight
+  uint32_t gdst = 0;
+  // Gather load j (chunk group j) of that tile.
+  auto gather = [&](int j) { load_to_lds16(gsrc + 64 * j, gdst + j * GROUP_BYTES); };
   for (int it = 0; it < ntiles; ++it) {
-    // Own loads: tile it (issued PREFETCH iterations ago) and the slot entries
-    // of tile it+PREFETCH (issued just after it) have landed.
-    wait_vmcnt<(PREFETCH - 1) * (CHUNK_GROUPS + 1)>();
+    // Own loads, issued in the order (per iteration i) slots of tile i+5,
+    // gather of tile i+3: tile it and, right after it, the slot entries of
+    // tile it+PREFETCH have landed once at most 19 younger loads are out.
+    wait_vmcnt<(PREFETCH - 1) * (CHUNK_GROUPS + 1) - 1>();
     lds_barrier();  // tile `it` complete; every wave is done with tile it-1's buffer
     const uint32_t cur = smem_base + (it % NBUF) * TILE_BYTES;
-    const int t_next = it + PREFETCH;
-    const uint16_t* gsrc = gather_src(ring_slot(t_next));
-    const uint32_t gdst = gather_dst(t_next);
-    issue_slots(t_next + 2);
-    // Gather load j (chunk group j) of tile t_next.
-    auto gather = [&](int j) { load_to_lds16(gsrc + 64 * j, gdst + j * GROUP_BYTES); };
 
-    // ---- S^T = K Q^T: 36 MFMAs (gather loads 0..4 ride along)
+    // ---- S^T = K Q^T: 36 MFMAs (gather loads 0..4 of tile it+PREFETCH ride along)
     f32x16 sv;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sv[i] = 0.f;
     {
-      auto kread = [&](int ks) { return lds_read_b128(cur + (ks >> 2) * GROUP_BYTES + qk_off[ks & 3]); };
+      // Per-tile base addresses; the chunk group goes into the instruction's
+      // immediate offset.
+      uint32_t qb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qb[j] = cur + qk_off[j];
+      auto kread = [&](int ks) { return lds_read_b128(qb[ks & 3] + (ks >> 2) * GROUP_BYTES); };
       bf16x8 kbuf[QK_AHEAD];
 #pragma unroll
       for (int ks = 0; ks < QK_AHEAD; ++ks) kbuf[ks] = kread(ks);
+      __builtin_amdgcn_sched_barrier(0);  // the operand reads go out before the slot read
+      const int t_next = it + PREFETCH;
+      const int slot_next = ring_slot(t_next);
+      gdst = gather_dst(t_next);
+      issue_slots(t_next + 2);
 #pragma unroll
       for (int ks = 0; ks < QK_STEPS; ++ks) {
         const bf16x8 kv = kbuf[ks % QK_AHEAD];
         if (ks + QK_AHEAD < QK_STEPS) kbuf[ks % QK_AHEAD] = kread(ks + QK_AHEAD);
         sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qf[ks], sv, 0, 0, 0);
+        if (ks == 2) gsrc = gather_src(slot_next);  // first needed at ks = 3
         if ((ks & 7) == 3) gather(ks >> 3);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -516,7 +526,8 @@ void verify_attn_partial_kernel(PartialArgs a) {
       for (int i = 0; i < 16; ++i) {
         const int key = kb0 + 8 * (i >> 2) + (i & 3);
         const int u = key - P;
-        const bool vis = key < k1 && (u < 0 || ((anc >> (u & 63)) & 1ull));
+        // bitwise, branch-free: the selects stay in place
+        const bool vis = (key < k1) & ((u < 0) | (((anc >> (u & 63)) & 1ull) != 0));
         sv[i] = vis ? sv[i] : -INFINITY;
       }
     }
@@ -554,11 +565,17 @@ void verify_attn_partial_kernel(PartialArgs a) {
     // ---- O^T += V^T P^T: 32 MFMAs (16 feature blocks x 2 key halves; gather
     // loads 5..8 ride along)
     {
+      uint32_t vb[2][2][2];  // per-tile base addresses (chunk group in the immediate offset)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int cp = 0; cp < 2; ++cp)
+#pragma unroll
+          for (int rd = 0; rd < 2; ++rd) vb[kh][cp][rd] = cur + pv_off[kh][cp][rd];
       auto vread = [&](int st) {  // step st = 2 cb + kh
         const int cb = st >> 1, kh = st & 1;
-        const uint32_t base = cur + (cb >> 1) * GROUP_BYTES;
-        const bf16x4 v0 = lds_read_tr(base + pv_off[kh][cb & 1][0]);
-        const bf16x4 v1 = lds_read_tr(base + pv_off[kh][cb & 1][1]);
+        const bf16x4 v0 = lds_read_tr(vb[kh][cb & 1][0] + (cb >> 1) * GROUP_BYTES);
+        const bf16x4 v1 = lds_read_tr(vb[kh][cb & 1][1] + (cb >> 1) * GROUP_BYTES);
         return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       };
       bf16x8 vbuf[PV_AHEAD];
