@@ -546,21 +546,10 @@ void verify_attn_partial_kernel(PartialArgs a) {
     }
     const float mu = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sv[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
+    for (int i = 0; i < 8; ++i) sv[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
     const bf16x8 pb0 = {(__bf16)sv[0], (__bf16)sv[1], (__bf16)sv[2], (__bf16)sv[3],
                         (__bf16)sv[4], (__bf16)sv[5], (__bf16)sv[6], (__bf16)sv[7]};
-    const bf16x8 pb1 = {(__bf16)sv[8], (__bf16)sv[9], (__bf16)sv[10], (__bf16)sv[11],
-                        (__bf16)sv[12], (__bf16)sv[13], (__bf16)sv[14], (__bf16)sv[15]};
-    {
-      // The running sum uses the same bf16-rounded weights that enter O.
-      const u32x4 w0 = __builtin_bit_cast(u32x4, pb0), w1 = __builtin_bit_cast(u32x4, pb1);
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc += (__builtin_bit_cast(float, w0[i] << 16) + __builtin_bit_cast(float, w0[i] & 0xffff0000u)) +
-               (__builtin_bit_cast(float, w1[i] << 16) + __builtin_bit_cast(float, w1[i] & 0xffff0000u));
-      l_run += acc;
-    }
+    bf16x8 pb1;
 
     // ---- O^T += V^T P^T: 32 MFMAs (16 feature blocks x 2 key halves; gather
     // loads 5..8 ride along)
@@ -572,8 +561,8 @@ void verify_attn_partial_kernel(PartialArgs a) {
         for (int cp = 0; cp < 2; ++cp)
 #pragma unroll
           for (int rd = 0; rd < 2; ++rd) vb[kh][cp][rd] = cur + pv_off[kh][cp][rd];
-      auto vread = [&](int st) {  // step st = 2 cb + kh
-        const int cb = st >> 1, kh = st & 1;
+      auto vread = [&](int st) {  // step st = 16 kh + cb
+        const int cb = st & 15, kh = st >> 4;
         const bf16x4 v0 = lds_read_tr(vb[kh][cb & 1][0] + (cb >> 1) * GROUP_BYTES);
         const bf16x4 v1 = lds_read_tr(vb[kh][cb & 1][1] + (cb >> 1) * GROUP_BYTES);
         return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -581,13 +570,27 @@ void verify_attn_partial_kernel(PartialArgs a) {
       bf16x8 vbuf[PV_AHEAD];
 #pragma unroll
       for (int st = 0; st < PV_AHEAD; ++st) vbuf[st] = vread(st);
-      mfma_valu_gap();  // pb0 / pb1 were just written by VALU instructions
+      mfma_valu_gap();  // pb0 was just written by VALU instructions
 #pragma unroll
       for (int st = 0; st < 2 * PV_BLOCKS; ++st) {
         const bf16x8 vt = vbuf[st % PV_AHEAD];
         if (st + PV_AHEAD < 2 * PV_BLOCKS) vbuf[st % PV_AHEAD] = vread(st + PV_AHEAD);
-        mfma_acc(o[st >> 1], vt, (st & 1) ? pb1 : pb0);
+        mfma_acc(o[st & 15], vt, st < 16 ? pb0 : pb1);
         if ((st & 7) == 5) gather(5 + (st >> 3));
+        if (st < 8) {
+          sv[8 + st] = __builtin_amdgcn_exp2f(sv[8 + st] - mu);
+        } else if (st == 8) {
+          pb1 = bf16x8{(__bf16)sv[8], (__bf16)sv[9], (__bf16)sv[10], (__bf16)sv[11],
+                       (__bf16)sv[12], (__bf16)sv[13], (__bf16)sv[14], (__bf16)sv[15]};
+        } else if (st == 9 || st == 10) {
+          // The running sum uses the same bf16-rounded weights that enter O.
+          const u32x4 w = __builtin_bit_cast(u32x4, st == 9 ? pb0 : pb1);
+          float acc = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc += __builtin_bit_cast(float, w[i] << 16) + __builtin_bit_cast(float, w[i] & 0xffff0000u);
+          l_run += acc;
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
