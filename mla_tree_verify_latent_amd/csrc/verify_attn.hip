@@ -298,7 +298,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 //   (c / 8) * 4096 + k * 128 + ((c % 8) ^ swz(k)) * 16.
 // Every wave gathers 8 rows of each tile: wave w loads KV rows 8w..8w+7 with 9
 // direct-to-LDS loads of 1 KB (one per chunk group), lane -> (row 8w + lane/8,
-// chunk position lane%8), spread over its MFMAs. The slot-table entries of
+// chunk position lane%8), spread over its QK MFMAs. The slot-table entries of
 // those rows travel global -> LDS as well (one 4-byte load per lane into a
 // small ring) two tiles before the gather that uses them. Past the end of the
 // split the loads repeat the split's last row, so each wave issues exactly 10
@@ -318,7 +318,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // Per tile: QK (36 MFMAs), the online softmax, PV (32 MFMAs). LDS buffers:
 // tile it in use, tiles it+1..it+3 in flight; one barrier per tile publishes
 // tile it and frees tile it-1's buffer for the gather of tile it+3, whose
-// nine loads ride on the MFMAs (five in QK, four in PV).
+// nine loads ride on the QK MFMAs (one every four).
 __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void verify_attn_partial_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * TILE_BYTES + SLOT_RING * NWAVES * 256];
@@ -485,7 +485,8 @@ void verify_attn_partial_kernel(PartialArgs a) {
     lds_barrier();  // tile `it` complete; every wave is done with tile it-1's buffer
     const uint32_t cur = smem_base + (it % NBUF) * TILE_BYTES;
 
-    // ---- S^T = K Q^T: 36 MFMAs (gather loads 0..4 of tile it+PREFETCH ride along)
+    // ---- S^T = K Q^T: 36 MFMAs (the nine gather loads of tile it+PREFETCH ride
+    // along, one every 4 MFMAs)
     f32x16 sv;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sv[i] = 0.f;
@@ -510,7 +511,7 @@ void verify_attn_partial_kernel(PartialArgs a) {
         if (ks + QK_AHEAD < QK_STEPS) kbuf[ks % QK_AHEAD] = kread(ks + QK_AHEAD);
         sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qf[ks], sv, 0, 0, 0);
         if (ks == 2) gsrc = gather_src(slot_next);  // first needed at ks = 3
-        if ((ks & 7) == 3) gather(ks >> 3);
+        if ((ks & 3) == 3) gather(ks >> 2);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -551,8 +552,7 @@ void verify_attn_partial_kernel(PartialArgs a) {
                         (__bf16)sv[4], (__bf16)sv[5], (__bf16)sv[6], (__bf16)sv[7]};
     bf16x8 pb1;
 
-    // ---- O^T += V^T P^T: 32 MFMAs (16 feature blocks x 2 key halves; gather
-    // loads 5..8 ride along)
+    // ---- O^T += V^T P^T: 32 MFMAs (16 feature blocks x 2 key halves)
     {
       uint32_t vb[2][2][2];  // per-tile base addresses (chunk group in the immediate offset)
 #pragma unroll
@@ -576,7 +576,6 @@ void verify_attn_partial_kernel(PartialArgs a) {
         const bf16x8 vt = vbuf[st % PV_AHEAD];
         if (st + PV_AHEAD < 2 * PV_BLOCKS) vbuf[st % PV_AHEAD] = vread(st + PV_AHEAD);
         mfma_acc(o[st & 15], vt, st < 16 ? pb0 : pb1);
-        if ((st & 7) == 5) gather(5 + (st >> 3));
         if (st < 8) {
           sv[8 + st] = __builtin_amdgcn_exp2f(sv[8 + st] - mu);
         } else if (st == 8) {
