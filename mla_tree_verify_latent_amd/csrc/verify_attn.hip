@@ -17,7 +17,7 @@
 //    head) pairs of one sequence, r = t*H + h) x one split of the sequence's
 //    KV positions; one workgroup per CU;
 //  - KV tiles of 32 rows (36 KB) are gathered straight into LDS with 16-byte
-//    direct-to-LDS loads, one slot-table lookup per row, three tiles ahead;
+//    direct-to-LDS loads, one slot-table lookup per row, two tiles ahead;
 //  - S^T = K Q^T and O^T += V^T P^T on MFMA 32x32x16 bf16, so every lane holds
 //    whole query rows of both the scores and the accumulator (the softmax state
 //    of a row never leaves its lane pair); V^T comes from the K-major LDS tile
@@ -49,13 +49,14 @@ constexpr int CHUNK_GROUPS = KV_DIM / 64;  // 9 groups of 64 bf16 (8 x 16 B) per
 constexpr int GROUP_BYTES = NK * 128;      // one group for all NK rows: 4 KB
 constexpr int TILE_BYTES = CHUNK_GROUPS * GROUP_BYTES;  // 36 KB
 constexpr int NBUF = 4;                    // LDS ring of KV tiles (144 KB)
-constexpr int PREFETCH = 3;                // tiles in flight beyond the one in use
+constexpr int PREFETCH = 2;                // tiles in flight beyond the two in use
 constexpr int SLOT_RING = 4;               // LDS ring of slot-table entries (tiles)
 constexpr int QK_STEPS = KV_DIM / 16;      // 36 MFMA k-steps of 16 features
 constexpr int PV_BLOCKS = V_DIM / 32;      // 16 output blocks of 32 features
 constexpr float LAZY_RESCALE_LOG2 = 8.0f;  // running max is raised only past +8 (base 2)
 constexpr int QK_AHEAD = 4;                // K operand reads in flight ahead of their MFMA
 constexpr int PV_AHEAD = 4;                // V^T operand reads in flight ahead
+constexpr int PV_SYNC_STEP = 15;           // PV step after which the next tile is published
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -316,9 +317,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // Each K or V^T operand read from LDS feeds 32 query rows.
 //
 // Per tile: QK (36 MFMAs), the online softmax, PV (32 MFMAs). LDS buffers:
-// tile it in use, tiles it+1..it+3 in flight; one barrier per tile publishes
-// tile it and frees tile it-1's buffer for the gather of tile it+3, whose
-// nine loads ride on the QK MFMAs (one every four).
+// tile it-1 (still read by slower waves), tile it in use, tiles it+1 and it+2
+// in flight. One barrier per tile, inside PV (after step PV_SYNC_STEP),
+// publishes tile it+1 and frees tile it-1's buffer for the gather of tile
+// it+3, whose nine loads ride on the next QK's MFMAs (one every four); the
+// first QK operand reads of tile it+1 are issued right after that barrier.
 __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void verify_attn_partial_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * TILE_BYTES + SLOT_RING * NWAVES * 256];
@@ -477,12 +480,20 @@ void verify_attn_partial_kernel(PartialArgs a) {
   uint32_t gdst = 0;
   // Gather load j (chunk group j) of that tile.
   auto gather = [&](int j) { load_to_lds16(gsrc + 64 * j, gdst + j * GROUP_BYTES); };
+  // The first QK operand reads of a tile are issued during the previous tile's
+  // PV, right after the barrier that publishes the tile.
+  bf16x8 kbuf[QK_AHEAD];
+  auto kread_tile = [&](uint32_t tile, int ks) {
+    return lds_read_b128(tile + qk_off[ks & 3] + (ks >> 2) * GROUP_BYTES);
+  };
+  // Own loads, issued in the order (per iteration i) slots of tile i+4, gather
+  // of tile i+2: tile t and the slot entries of tile t+2 (issued before the
+  // gather of tile t+1) have landed once at most 10 younger loads are out.
+  wait_vmcnt<CHUNK_GROUPS + 1>();
+  lds_barrier();  // tile 0 complete; ancestor masks visible
+#pragma unroll
+  for (int ks = 0; ks < QK_AHEAD; ++ks) kbuf[ks] = kread_tile(smem_base, ks);
   for (int it = 0; it < ntiles; ++it) {
-    // Own loads, issued in the order (per iteration i) slots of tile i+5,
-    // gather of tile i+3: tile it and, right after it, the slot entries of
-    // tile it+PREFETCH have landed once at most 19 younger loads are out.
-    wait_vmcnt<(PREFETCH - 1) * (CHUNK_GROUPS + 1) - 1>();
-    lds_barrier();  // tile `it` complete; every wave is done with tile it-1's buffer
     const uint32_t cur = smem_base + (it % NBUF) * TILE_BYTES;
 
     // ---- S^T = K Q^T: 36 MFMAs (the nine gather loads of tile it+PREFETCH ride
@@ -497,10 +508,6 @@ void verify_attn_partial_kernel(PartialArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) qb[j] = cur + qk_off[j];
       auto kread = [&](int ks) { return lds_read_b128(qb[ks & 3] + (ks >> 2) * GROUP_BYTES); };
-      bf16x8 kbuf[QK_AHEAD];
-#pragma unroll
-      for (int ks = 0; ks < QK_AHEAD; ++ks) kbuf[ks] = kread(ks);
-      __builtin_amdgcn_sched_barrier(0);  // the operand reads go out before the slot read
       const int t_next = it + PREFETCH;
       const int slot_next = ring_slot(t_next);
       gdst = gather_dst(t_next);
@@ -576,6 +583,16 @@ void verify_attn_partial_kernel(PartialArgs a) {
         const bf16x8 vt = vbuf[st % PV_AHEAD];
         if (st + PV_AHEAD < 2 * PV_BLOCKS) vbuf[st % PV_AHEAD] = vread(st + PV_AHEAD);
         mfma_acc(o[st & 15], vt, st < 16 ? pb0 : pb1);
+        if (st == PV_SYNC_STEP && it + 1 < ntiles) {
+          // Publish tile it+1: own part landed, then the workgroup barrier.
+          // Every wave is past the PV of tile it-1 here, so the gather issued
+          // in the next QK may overwrite that tile's buffer. No LDS-read wait
+          // is needed: the reads still in flight are of tile it.
+          wait_vmcnt<CHUNK_GROUPS + 1>();
+          asm volatile("s_barrier" ::: "memory");
+        }
+        if (st > PV_SYNC_STEP && st <= PV_SYNC_STEP + QK_AHEAD && it + 1 < ntiles)
+          kbuf[st - PV_SYNC_STEP - 1] = kread_tile(smem_base + ((it + 1) % NBUF) * TILE_BYTES, st - PV_SYNC_STEP - 1);
         if (st < 8) {
           sv[8 + st] = __builtin_amdgcn_exp2f(sv[8 + st] - mu);
         } else if (st == 8) {
