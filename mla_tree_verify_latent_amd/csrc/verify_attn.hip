@@ -49,14 +49,13 @@ constexpr int CHUNK_GROUPS = KV_DIM / 64;  // 9 groups of 64 bf16 (8 x 16 B) per
 constexpr int GROUP_BYTES = NK * 128;      // one group for all NK rows: 4 KB
 constexpr int TILE_BYTES = CHUNK_GROUPS * GROUP_BYTES;  // 36 KB
 constexpr int NBUF = 4;                    // LDS ring of KV tiles (144 KB)
-constexpr int PREFETCH = 2;                // tiles in flight beyond the two in use
 constexpr int SLOT_RING = 4;               // LDS ring of slot-table entries (tiles)
 constexpr int QK_STEPS = KV_DIM / 16;      // 36 MFMA k-steps of 16 features
 constexpr int PV_BLOCKS = V_DIM / 32;      // 16 output blocks of 32 features
 constexpr float LAZY_RESCALE_LOG2 = 8.0f;  // running max is raised only past +8 (base 2)
 constexpr int QK_AHEAD = 4;                // K operand reads in flight ahead of their MFMA
 constexpr int PV_AHEAD = 4;                // V^T operand reads in flight ahead
-constexpr int PV_SYNC_STEP = 15;           // PV step after which the next tile is published
+constexpr int SM_PIECES = 16;              // softmax pieces interleaved with the next QK
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -316,12 +315,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 //     holds row r = l%32, features 32cb + 8(i/4) + 4(l/32) + i%4.
 // Each K or V^T operand read from LDS feeds 32 query rows.
 //
-// Per tile: QK (36 MFMAs), the online softmax, PV (32 MFMAs). LDS buffers:
-// tile it-1 (still read by slower waves), tile it in use, tiles it+1 and it+2
-// in flight. One barrier per tile, inside PV (after step PV_SYNC_STEP),
-// publishes tile it+1 and frees tile it-1's buffer for the gather of tile
-// it+3, whose nine loads ride on the next QK's MFMAs (one every four); the
-// first QK operand reads of tile it+1 are issued right after that barrier.
+// Software pipeline: iteration `it` runs the QK of tile it+1 (36 MFMAs) with
+// the online softmax of tile it issued between its MFMAs, then the PV of tile
+// it (32 MFMAs). A raised running max rescales O after PV(it-1), as the online
+// softmax requires. LDS buffers: tile it (PV), tile it+1 (QK), tiles it+2 and
+// it+3 in flight. One barrier per iteration publishes tile it+1 and, every
+// wave being done with iteration it-1, frees tile it-1's buffer for the gather
+// of tile it+3, whose nine loads ride on the QK MFMAs (one every four).
 __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void verify_attn_partial_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * TILE_BYTES + SLOT_RING * NWAVES * 256];
@@ -458,16 +458,16 @@ void verify_attn_partial_kernel(PartialArgs a) {
 
 
   const int ntiles = (k1 - k0 + NK - 1) / NK;
-  // Prologue: the slot entries of tiles 0..PREFETCH-1 come straight into
-  // registers; then the steady-state load order (iteration i: slots of tile
-  // i + PREFETCH + 2, gather of tile i + PREFETCH) for i = -PREFETCH .. -1.
+  // Prologue: the slot entries of tiles 0 and 1 come straight into registers;
+  // then the steady-state load order (iteration i: slots of tile i+5, gather of
+  // tile i+3) for i = -3, -2 (the gathers of tiles 0 and 1).
   {
-    int s[PREFETCH];
+    int s[2];
 #pragma unroll
-    for (int t = 0; t < PREFETCH; ++t) s[t] = *slot_ptr(k0 + t * NK, lane >> 3);
+    for (int t = 0; t < 2; ++t) s[t] = *slot_ptr(k0 + t * NK, lane >> 3);
     wait_vmcnt<0>();  // query, slot and tree loads done before the asm loads start
 #pragma unroll
-    for (int t = 0; t < PREFETCH; ++t) {
+    for (int t = 0; t < 2; ++t) {
       issue_slots(t + 2);
       const uint16_t* src = gather_src(s[t]);
       const uint32_t dst = gather_dst(t);
@@ -476,140 +476,156 @@ void verify_attn_partial_kernel(PartialArgs a) {
     }
   }
 
-  const uint16_t* gsrc = a.kv;  // gather source / destination of the tile in flight
-  uint32_t gdst = 0;
-  // Gather load j (chunk group j) of that tile.
-  auto gather = [&](int j) { load_to_lds16(gsrc + 64 * j, gdst + j * GROUP_BYTES); };
-  // The first QK operand reads of a tile are issued during the previous tile's
-  // PV, right after the barrier that publishes the tile.
-  bf16x8 kbuf[QK_AHEAD];
-  auto kread_tile = [&](uint32_t tile, int ks) {
-    return lds_read_b128(tile + qk_off[ks & 3] + (ks >> 2) * GROUP_BYTES);
-  };
-  // Own loads, issued in the order (per iteration i) slots of tile i+4, gather
-  // of tile i+2: tile t and the slot entries of tile t+2 (issued before the
-  // gather of tile t+1) have landed once at most 10 younger loads are out.
-  wait_vmcnt<CHUNK_GROUPS + 1>();
-  lds_barrier();  // tile 0 complete; ancestor masks visible
+  // ---- online softmax (base 2) of one tile's scores `sv`, in pieces that run
+  // between the MFMAs of the next tile's QK. Piece st < SM_PIECES.
+  f32x16 sv;                  // scores of the tile, then its weights
+  int sm_kt = 0;              // first key of the tile
+  float mx = 0.f, alpha = 1.f;
+  bool any_raise = false;
+  bf16x8 pb0 = {}, pb1 = {};  // bf16 weights: the PV B operand for keys of i < 8 / i >= 8
+  auto sm_piece = [&](int st) __attribute__((always_inline)) {
+    if (st == 0) {
 #pragma unroll
-  for (int ks = 0; ks < QK_AHEAD; ++ks) kbuf[ks] = kread_tile(smem_base, ks);
-  for (int it = 0; it < ntiles; ++it) {
-    const uint32_t cur = smem_base + (it % NBUF) * TILE_BYTES;
-
-    // ---- S^T = K Q^T: 36 MFMAs (the nine gather loads of tile it+PREFETCH ride
-    // along, one every 4 MFMAs)
-    f32x16 sv;
+      for (int i = 0; i < 16; ++i) sv[i] *= a.qk_scale_log2;
+    } else if (st == 1) {
+      if (sm_kt + NK > k1 || sm_kt + NK > P) {  // the tile reaches the split end or the tree
+        const unsigned long long anc = anc_s[row_ok ? qrow / a.H : 0];
+        const int kb0 = sm_kt + 4 * hl;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sv[i] = 0.f;
-    {
-      // Per-tile base addresses; the chunk group goes into the instruction's
-      // immediate offset.
-      uint32_t qb[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) qb[j] = cur + qk_off[j];
-      auto kread = [&](int ks) { return lds_read_b128(qb[ks & 3] + (ks >> 2) * GROUP_BYTES); };
-      const int t_next = it + PREFETCH;
-      const int slot_next = ring_slot(t_next);
-      gdst = gather_dst(t_next);
-      issue_slots(t_next + 2);
-#pragma unroll
-      for (int ks = 0; ks < QK_STEPS; ++ks) {
-        const bf16x8 kv = kbuf[ks % QK_AHEAD];
-        if (ks + QK_AHEAD < QK_STEPS) kbuf[ks % QK_AHEAD] = kread(ks + QK_AHEAD);
-        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qf[ks], sv, 0, 0, 0);
-        if (ks == 2) gsrc = gather_src(slot_next);  // first needed at ks = 3
-        if ((ks & 3) == 3) gather(ks >> 2);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb0 + 8 * (i >> 2) + (i & 3);
+          const int u = key - P;
+          // bitwise, branch-free: the selects stay in place
+          const bool vis = (key < k1) & ((u < 0) | (((anc >> (u & 63)) & 1ull) != 0));
+          sv[i] = vis ? sv[i] : -INFINITY;
+        }
       }
-    }
-
-    // ---- scale, tree mask, online softmax (base 2)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sv[i] *= a.qk_scale_log2;
-    const int kt = k0 + it * NK;
-    if (kt + NK > k1 || kt + NK > P) {  // the tile reaches the split end or the tree
-      const unsigned long long anc = anc_s[row_ok ? qrow / a.H : 0];
-      const int kb0 = kt + 4 * hl;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb0 + 8 * (i >> 2) + (i & 3);
-        const int u = key - P;
-        // bitwise, branch-free: the selects stay in place
-        const bool vis = (key < k1) & ((u < 0) | (((anc >> (u & 63)) & 1ull) != 0));
-        sv[i] = vis ? sv[i] : -INFINITY;
-      }
-    }
-    float mx = fmaxf(fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7]))),
-                     fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])), fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
-    mx = fmaxf(mx, xor32(mx));  // lanes l and l^32 hold the same query row
-    const bool raise = mx > m_run + LAZY_RESCALE_LOG2;
-    if (__ballot(raise)) {
-      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;  // m_run = -inf -> 0
+    } else if (st == 2) {
+      mx = fmaxf(fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7]))),
+                 fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])), fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+    } else if (st == 3) {
+      mx = fmaxf(mx, xor32(mx));  // lanes l and l^32 hold the same query row
+      const bool raise = mx > m_run + LAZY_RESCALE_LOG2;
+      any_raise = __ballot(raise) != 0;
+      alpha = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;  // m_run = -inf -> 0
       m_run = raise ? mx : m_run;
       l_run *= alpha;
+    } else if (st < 12) {
+      const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+      const int i = 2 * (st - 4);
+      sv[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
+      sv[i + 1] = __builtin_amdgcn_exp2f(sv[i + 1] - mu);
+    } else if (st == 12) {
+      pb0 = bf16x8{(__bf16)sv[0], (__bf16)sv[1], (__bf16)sv[2], (__bf16)sv[3],
+                   (__bf16)sv[4], (__bf16)sv[5], (__bf16)sv[6], (__bf16)sv[7]};
+    } else if (st == 13) {
+      pb1 = bf16x8{(__bf16)sv[8], (__bf16)sv[9], (__bf16)sv[10], (__bf16)sv[11],
+                   (__bf16)sv[12], (__bf16)sv[13], (__bf16)sv[14], (__bf16)sv[15]};
+    } else if (st == 14 || st == 15) {
+      // The running sum uses the same bf16-rounded weights that enter O.
+      const u32x4 w = __builtin_bit_cast(u32x4, st == 14 ? pb0 : pb1);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc += __builtin_bit_cast(float, w[i] << 16) + __builtin_bit_cast(float, w[i] & 0xffff0000u);
+      l_run += acc;
+    }
+  };
+
+  // ---- S^T = K Q^T for tile t: 36 MFMAs, with the nine gather loads of tile
+  // t+2 (one every 4 MFMAs) and, when `with_softmax`, the softmax pieces of
+  // the previous tile (one every 2 MFMAs) in between.
+  auto qk_tile = [&](int t, bool with_softmax) __attribute__((always_inline)) {
+    const uint32_t cur = smem_base + (t % NBUF) * TILE_BYTES;
+    uint32_t qb[4];  // per-tile base addresses; the chunk group goes in the immediate offset
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qb[j] = cur + qk_off[j];
+    auto kread = [&](int ks) { return lds_read_b128(qb[ks & 3] + (ks >> 2) * GROUP_BYTES); };
+    bf16x8 kbuf[QK_AHEAD];
+#pragma unroll
+    for (int ks = 0; ks < QK_AHEAD; ++ks) kbuf[ks] = kread(ks);
+    __builtin_amdgcn_sched_barrier(0);  // the operand reads go out before the slot read
+    const int slot_next = ring_slot(t + 2);
+    const uint32_t gdst = gather_dst(t + 2);
+    issue_slots(t + 4);
+    const uint16_t* gsrc = a.kv;
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < QK_STEPS; ++ks) {
+      const bf16x8 kv = kbuf[ks % QK_AHEAD];
+      if (ks + QK_AHEAD < QK_STEPS) kbuf[ks % QK_AHEAD] = kread(ks + QK_AHEAD);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qf[ks], s, 0, 0, 0);
+      if (ks == 2) gsrc = gather_src(slot_next);  // first needed at ks = 3
+      if ((ks & 3) == 3) load_to_lds16(gsrc + 64 * (ks >> 2), gdst + (ks >> 2) * GROUP_BYTES);
+      if (with_softmax && (ks & 1) == 0 && (ks >> 1) < SM_PIECES) sm_piece(ks >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return s;
+  };
+
+  // ---- O^T += V^T P^T for tile t: 32 MFMAs, key half 0 (B = pb0) over the
+  // 16 feature blocks, then key half 1 (B = pb1).
+  auto pv_tile = [&](int t) __attribute__((always_inline)) {
+    const uint32_t cur = smem_base + (t % NBUF) * TILE_BYTES;
+    uint32_t vb[2][2][2];  // per-tile base addresses (chunk group in the immediate offset)
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int cp = 0; cp < 2; ++cp)
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) vb[kh][cp][rd] = cur + pv_off[kh][cp][rd];
+    auto vread = [&](int st) {  // step st = 16 kh + cb
+      const int cb = st & 15, kh = st >> 4;
+      const bf16x4 v0 = lds_read_tr(vb[kh][cb & 1][0] + (cb >> 1) * GROUP_BYTES);
+      const bf16x4 v1 = lds_read_tr(vb[kh][cb & 1][1] + (cb >> 1) * GROUP_BYTES);
+      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 vbuf[PV_AHEAD];
+#pragma unroll
+    for (int st = 0; st < PV_AHEAD; ++st) vbuf[st] = vread(st);
+    mfma_valu_gap();  // pb0 / pb1 were written by VALU instructions
+#pragma unroll
+    for (int st = 0; st < 2 * PV_BLOCKS; ++st) {
+      const bf16x8 vt = vbuf[st % PV_AHEAD];
+      if (st + PV_AHEAD < 2 * PV_BLOCKS) vbuf[st % PV_AHEAD] = vread(st + PV_AHEAD);
+      mfma_acc(o[st & 15], vt, st < 16 ? pb0 : pb1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Tile 0: publish it (own loads of tile 0 and the slots of tile 2 landed),
+  // then its QK (carrying the gather of tile 2).
+  wait_vmcnt<CHUNK_GROUPS + 1>();
+  lds_barrier();  // tile 0 complete; ancestor masks visible
+  sv = qk_tile(0, false);
+  // Iteration it: QK of tile it+1 with the softmax of tile it in between, then
+  // PV of tile it. Own loads are issued in the order (iteration i) slots of
+  // tile i+5, gather of tile i+3; at the top of iteration it the gather of
+  // tile it+1 and, before it, the slots of tile it+3 have landed once at most
+  // 10 younger loads are out. The barrier publishes tile it+1 and, every wave
+  // being done with iteration it-1, frees tile it-1's buffer for the gather of
+  // tile it+3.
+  for (int it = 0; it < ntiles; ++it) {
+    sm_kt = k0 + it * NK;
+    f32x16 sn;
+    if (it + 1 < ntiles) {
+      wait_vmcnt<CHUNK_GROUPS + 1>();
+      lds_barrier();
+      sn = qk_tile(it + 1, true);
+    } else {
+#pragma unroll
+      for (int st = 0; st < SM_PIECES; ++st) sm_piece(st);
+    }
+    if (any_raise) {  // O (PV up to tile it-1) *= alpha
       mfma_drain();
 #pragma unroll
       for (int cb = 0; cb < PV_BLOCKS; ++cb) acc_scale(o[cb], alpha);
       mfma_valu_gap();
     }
-    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sv[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
-    const bf16x8 pb0 = {(__bf16)sv[0], (__bf16)sv[1], (__bf16)sv[2], (__bf16)sv[3],
-                        (__bf16)sv[4], (__bf16)sv[5], (__bf16)sv[6], (__bf16)sv[7]};
-    bf16x8 pb1;
-
-    // ---- O^T += V^T P^T: 32 MFMAs (16 feature blocks x 2 key halves)
-    {
-      uint32_t vb[2][2][2];  // per-tile base addresses (chunk group in the immediate offset)
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int cp = 0; cp < 2; ++cp)
-#pragma unroll
-          for (int rd = 0; rd < 2; ++rd) vb[kh][cp][rd] = cur + pv_off[kh][cp][rd];
-      auto vread = [&](int st) {  // step st = 16 kh + cb
-        const int cb = st & 15, kh = st >> 4;
-        const bf16x4 v0 = lds_read_tr(vb[kh][cb & 1][0] + (cb >> 1) * GROUP_BYTES);
-        const bf16x4 v1 = lds_read_tr(vb[kh][cb & 1][1] + (cb >> 1) * GROUP_BYTES);
-        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      bf16x8 vbuf[PV_AHEAD];
-#pragma unroll
-      for (int st = 0; st < PV_AHEAD; ++st) vbuf[st] = vread(st);
-      mfma_valu_gap();  // pb0 was just written by VALU instructions
-#pragma unroll
-      for (int st = 0; st < 2 * PV_BLOCKS; ++st) {
-        const bf16x8 vt = vbuf[st % PV_AHEAD];
-        if (st + PV_AHEAD < 2 * PV_BLOCKS) vbuf[st % PV_AHEAD] = vread(st + PV_AHEAD);
-        mfma_acc(o[st & 15], vt, st < 16 ? pb0 : pb1);
-        if (st == PV_SYNC_STEP && it + 1 < ntiles) {
-          // Publish tile it+1: own part landed, then the workgroup barrier.
-          // Every wave is past the PV of tile it-1 here, so the gather issued
-          // in the next QK may overwrite that tile's buffer. No LDS-read wait
-          // is needed: the reads still in flight are of tile it.
-          wait_vmcnt<CHUNK_GROUPS + 1>();
-          asm volatile("s_barrier" ::: "memory");
-        }
-        if (st > PV_SYNC_STEP && st <= PV_SYNC_STEP + QK_AHEAD && it + 1 < ntiles)
-          kbuf[st - PV_SYNC_STEP - 1] = kread_tile(smem_base + ((it + 1) % NBUF) * TILE_BYTES, st - PV_SYNC_STEP - 1);
-        if (st < 8) {
-          sv[8 + st] = __builtin_amdgcn_exp2f(sv[8 + st] - mu);
-        } else if (st == 8) {
-          pb1 = bf16x8{(__bf16)sv[8], (__bf16)sv[9], (__bf16)sv[10], (__bf16)sv[11],
-                       (__bf16)sv[12], (__bf16)sv[13], (__bf16)sv[14], (__bf16)sv[15]};
-        } else if (st == 9 || st == 10) {
-          // The running sum uses the same bf16-rounded weights that enter O.
-          const u32x4 w = __builtin_bit_cast(u32x4, st == 9 ? pb0 : pb1);
-          float acc = 0.f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc += __builtin_bit_cast(float, w[i] << 16) + __builtin_bit_cast(float, w[i] & 0xffff0000u);
-          l_run += acc;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    pv_tile(it);
+    sv = sn;
   }
   wait_vmcnt<0>();  // no load outlives the workgroup
   mfma_drain();     // O is read below
