@@ -356,39 +356,6 @@ void verify_attn_partial_kernel(PartialArgs a) {
   const int k1 = min(k0 + a.chunk, loc.len);
   const int P = loc.len - a.T;
 
-  // Ancestor masks of this sequence's tree (bit u of anc[t]: node u is t or an
-  // ancestor of t). Parent pointers outside [-1, u-1] end the walk.
-  if (threadIdx.x < a.T) {
-    const int32_t* par = a.tree_parent + (int64_t)loc.b * a.T;
-    unsigned long long m = 0;
-    int u = threadIdx.x;
-    for (int step = 0; step < a.T && u >= 0; ++step) {
-      m |= 1ull << u;
-      const int p = par[u];
-      u = (p < u) ? p : -1;
-    }
-    anc_s[threadIdx.x] = m;
-  }
-
-  // Query fragments (B operand of S^T = K Q^T): lane l holds row l%32,
-  // features 16 ks + 8 (l/32) .. +7 of k-step ks. Waves without query rows
-  // run the same schedule on zeros (they still gather their share of the KV).
-  const int row0 = rt * ROWS_PER_TILE + wave * ROWS_PER_WAVE;
-  const bool wave_active = row0 < a.M;  // wave-uniform
-  const int qrow = row0 + (lane & 31);
-  const bool row_ok = qrow < a.M;
-  const int hl = lane >> 5;  // lane half
-  bf16x8 qf[QK_STEPS];
-  {
-    const uint16_t* src = a.q + ((int64_t)loc.b * a.M + (row_ok ? qrow : 0)) * KV_DIM + 8 * hl;
-#pragma unroll
-    for (int ks = 0; ks < QK_STEPS; ++ks) {
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (row_ok) v = *reinterpret_cast<const u32x4*>(src + 16 * ks);
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
   // ---- KV gather addressing
   const int ld_row = wave * ROWS_PER_LOAD_WAVE + (lane >> 3);
   const int ld_elem = 8 * ((lane & 7) ^ swz(ld_row));
@@ -419,6 +386,68 @@ void verify_attn_partial_kernel(PartialArgs a) {
   auto gather_dst = [&](int t) {
     return smem_base + (t % NBUF) * TILE_BYTES + wave * (ROWS_PER_LOAD_WAVE * 128);
   };
+
+  // Prologue loads, oldest first: the slot entries of tiles 0 and 1 (lane: row
+  // lane/8 of this wave's 8), the tree's parent pointers (wave 0), the query
+  // fragments. The gathers of tiles 0 and 1 start as soon as the slot entries
+  // are in, while the query loads are still on their way.
+  int s_pro[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) s_pro[t] = *slot_ptr(k0 + t * NK, lane >> 3);
+  int parent = -1;
+  if (wave == 0 && lane < a.T) parent = a.tree_parent[(int64_t)loc.b * a.T + lane];
+  // Query fragments (B operand of S^T = K Q^T): lane l holds row l%32,
+  // features 16 ks + 8 (l/32) .. +7 of k-step ks. Waves without query rows
+  // run the same schedule on zeros (they still gather their share of the KV).
+  const int row0 = rt * ROWS_PER_TILE + wave * ROWS_PER_WAVE;
+  const bool wave_active = row0 < a.M;  // wave-uniform
+  const int qrow = row0 + (lane & 31);
+  const bool row_ok = qrow < a.M;
+  const int hl = lane >> 5;  // lane half
+  bf16x8 qf[QK_STEPS];
+  {
+    const uint16_t* src = a.q + ((int64_t)loc.b * a.M + (row_ok ? qrow : 0)) * KV_DIM + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < QK_STEPS; ++ks) {
+      // Unconditional load (rows past M read row 0, which exists), then a
+      // select: no branches, so the waits for the slot entries stay exact.
+      u32x4 v = *reinterpret_cast<const u32x4*>(src + 16 * ks);
+      if (!row_ok) v = u32x4{0u, 0u, 0u, 0u};
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  // Steady-state load order (iteration i: slots of tile i+5, gather of tile
+  // i+3) for i = -3, -2: the gathers of tiles 0 and 1.
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    issue_slots(t + 2);
+    const uint16_t* src = gather_src(s_pro[t]);
+    const uint32_t dst = gather_dst(t);
+#pragma unroll
+    for (int j = 0; j < CHUNK_GROUPS; ++j) load_to_lds16(src + 64 * j, dst + j * GROUP_BYTES);
+  }
+
+  // Ancestor masks of this sequence's tree (bit u of anc[t]: node u is t or an
+  // ancestor of t), by pointer jumping over the lanes of wave 0: after round k
+  // a node's mask holds its ancestors within distance 2^(k+1) - 1, and up[t]
+  // is its ancestor at distance 2^(k+1) (or -1). Six rounds cover depth 63.
+  // Parent pointers outside [-1, t-1] make t a root.
+  if (wave == 0) {
+    int up = (parent >= 0 && parent < lane && lane < a.T) ? parent : -1;
+    unsigned long long m = lane < a.T ? (1ull << lane) : 0ull;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const int src = up >= 0 ? up : lane;
+      const unsigned long long m_up = __shfl(m, src);
+      const int up_up = __shfl(up, src);
+      if (up >= 0) {
+        m |= m_up;
+        up = up_up;
+      }
+    }
+    if (lane < a.T) anc_s[lane] = m;
+  }
 
   // Operand read offsets inside a tile (the chunk group is added as a constant).
   //  QK k-step ks reads chunk 2 ks + l/32 of key row l%32: group ks/4,
@@ -458,24 +487,6 @@ void verify_attn_partial_kernel(PartialArgs a) {
 
 
   const int ntiles = (k1 - k0 + NK - 1) / NK;
-  // Prologue: the slot entries of tiles 0 and 1 come straight into registers;
-  // then the steady-state load order (iteration i: slots of tile i+5, gather of
-  // tile i+3) for i = -3, -2 (the gathers of tiles 0 and 1).
-  {
-    int s[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) s[t] = *slot_ptr(k0 + t * NK, lane >> 3);
-    wait_vmcnt<0>();  // query, slot and tree loads done before the asm loads start
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      issue_slots(t + 2);
-      const uint16_t* src = gather_src(s[t]);
-      const uint32_t dst = gather_dst(t);
-#pragma unroll
-      for (int j = 0; j < CHUNK_GROUPS; ++j) load_to_lds16(src + 64 * j, dst + j * GROUP_BYTES);
-    }
-  }
-
   // ---- online softmax (base 2) of one tile's scores `sv`, in pieces that run
   // between the MFMAs of the next tile's QK. Piece st < SM_PIECES.
   f32x16 sv;                  // scores of the tile, then its weights
