@@ -91,6 +91,7 @@ class Bench:
                 d["q"] = base["q"].clone()
             self.reps.append(d)
         self.out = torch.empty((wl.B, wl.T, wl.H, 512), dtype=torch.bfloat16, device="cuda")
+        self.kv_new = torch.zeros((wl.B, wl.T, 576), dtype=torch.bfloat16, device="cuda")
         torch.cuda.synchronize()
 
     def call(self, r, stage="full"):
@@ -103,6 +104,9 @@ class Bench:
                                          d["tree_parent"], self.ws, self.params)
         elif stage == "combine":
             self.mtv.verify_attn_combine(d["seq_lens"], self.out, self.ws, self.params)
+        elif stage == "append":  # draft-row KV append (writes the tree rows of the pool)
+            self.mtv.verify_attn_append_kv(self.kv_new, d["slot_idx"], d["seq_lens"], d["kv_pool"],
+                                           self.params)
 
     def graph(self, n, stage):
         torch = self.torch
@@ -297,7 +301,7 @@ def main():
         print(json.dumps({"stage": args.stage, "workload": args.workload, "calls": args.warmup + args.steps}))
         return
 
-    head = measure(args.workload, args.steps, args.warmup)
+    head = measure(args.workload, args.steps, args.warmup, stages=("full", "partial", "append"))
     ms = head["full_ms"]
     gbs = head["bytes"] / (ms * 1e-3) / 1e9
     part_ms = head["partial_ms"]
@@ -353,6 +357,12 @@ def main():
             "traffic": traffic_from_counters(part_ms),
         },
         "extras": extras,
+        # draft-row KV append on the same workload: B*T rows of 1,152 B read and written
+        "append_kv": {
+            "rows": head["wl"].B * head["wl"].T,
+            "us_per_call": round(head["append_ms"] * 1e3, 2),
+            "gbs": round(2 * KV_ROW_BYTES * head["wl"].B * head["wl"].T / (head["append_ms"] * 1e-3) / 1e9, 1),
+        },
     }
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args.workload)

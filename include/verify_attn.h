@@ -147,13 +147,33 @@ typedef struct verify_attn_plan_info {
 
 int verify_attn_plan(const verify_attn_params* p, verify_attn_plan_info* info);
 
+/*
+ * Draft-row KV append: the step right before verify in the extend layout,
+ * where the draft tokens' own KV slots follow each sequence's prefix slots
+ * ("The Checkpoint Report", Mistakes and Incorrect Assumptions). Row (b, t) of
+ * kv_new (the latent row of draft-tree node t of sequence b) is copied to
+ *   kv_pool[slot_idx[seg_b + seq_lens[b] - T + t]],   seg_b = sum_{b' < b} seq_lens[b'],
+ * so that a following verify_attn on the same stream sees the tree nodes' rows.
+ * Uses num_seqs, tree_size, max_seq_len, total_kv and pool_slots of `p` (the
+ * params of the verify call it precedes; the same validation applies).
+ *   kv_new   bf16 [B, T, 576], contiguous, 16-byte aligned (read)
+ *   slot_idx, seq_lens as for verify_attn (read)
+ *   kv_pool  bf16 [pool_slots, 576], 16-byte aligned; the B*T target rows are written
+ * Enqueued on `stream`; no allocation and no host synchronisation, so it can be
+ * recorded in the same HIP graph as the verify call. Slots outside
+ * [0, pool_slots) are skipped; if two nodes share a slot, which row lands is
+ * unspecified. Status codes as above.
+ */
+int verify_attn_append_kv(const verify_attn_params* p, const void* kv_new, const int32_t* slot_idx,
+                          const int32_t* seq_lens, void* kv_pool, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* verify_attn_strerror(int status);
 
-/* ABI version of this header: (major << 16) | minor. */
+/* ABI version of this header: (major << 16) | minor (minor 1: verify_attn_append_kv). */
 int verify_attn_version(void);
 
-#define VERIFY_ATTN_VERSION ((1 << 16) | 0)
+#define VERIFY_ATTN_VERSION ((1 << 16) | 1)
 
 #ifdef __cplusplus
 }

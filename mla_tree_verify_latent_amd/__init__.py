@@ -8,8 +8,8 @@ raise.
 
 Entry points mirror the C ABI declared in ``include/verify_attn.h``:
 ``verify_attn``, ``verify_attn_partial``, ``verify_attn_combine``,
-``verify_attn_workspace_size``, ``verify_attn_plan``, ``verify_attn_strerror``,
-``verify_attn_version``.
+``verify_attn_append_kv``, ``verify_attn_workspace_size``, ``verify_attn_plan``,
+``verify_attn_strerror``, ``verify_attn_version``.
 """
 from __future__ import annotations
 
@@ -25,7 +25,8 @@ V_DIM = 512
 MAX_TREE = 64
 
 EXPORTS = (
-    "verify_attn", "verify_attn_partial", "verify_attn_combine", "verify_attn_workspace_size",
+    "verify_attn", "verify_attn_partial", "verify_attn_combine", "verify_attn_append_kv",
+    "verify_attn_workspace_size",
     "verify_attn_plan", "verify_attn_strerror", "verify_attn_version",
 )
 
@@ -78,6 +79,8 @@ def load_library(path: str = LIB_PATH):
     lib.verify_attn_partial.restype = ctypes.c_int
     lib.verify_attn_combine.argtypes = [P, i32p, vp, vp, ctypes.c_size_t, vp]
     lib.verify_attn_combine.restype = ctypes.c_int
+    lib.verify_attn_append_kv.argtypes = [P, vp, i32p, i32p, vp, vp]
+    lib.verify_attn_append_kv.restype = ctypes.c_int
     lib.verify_attn_plan.argtypes = [P, ctypes.POINTER(PlanInfo)]
     lib.verify_attn_plan.restype = ctypes.c_int
     lib.verify_attn_strerror.argtypes = [ctypes.c_int]
@@ -190,6 +193,26 @@ def verify_attn_combine(seq_lens, out, workspace, params: Params, stream=None) -
     _check(load_library().verify_attn_combine(
         ctypes.byref(params), _ptr(seq_lens), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def verify_attn_append_kv(kv_new, slot_idx, seq_lens, kv_pool, params: Params, stream=None) -> None:
+    """Enqueue the draft-row KV append: kv_new [B, T, 576] -> kv_pool at the
+    tree nodes' slots (the last T entries of each sequence's slot_idx segment)."""
+    import torch
+    for name, t in dict(kv_new=kv_new, slot_idx=slot_idx, seq_lens=seq_lens, kv_pool=kv_pool).items():
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if kv_new.dtype != torch.bfloat16 or kv_pool.dtype != torch.bfloat16:
+        raise ValueError("kv_new and kv_pool must be bfloat16")
+    if slot_idx.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("slot_idx and seq_lens must be int32")
+    if tuple(kv_new.shape) != (params.num_seqs, params.tree_size, KV_DIM):
+        raise ValueError("kv_new must be [B, T, 576]")
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != KV_DIM:
+        raise ValueError("kv_pool must be [slots, 576]")
+    _check(load_library().verify_attn_append_kv(
+        ctypes.byref(params), _ptr(kv_new), _ptr(slot_idx), _ptr(seq_lens), _ptr(kv_pool),
+        _stream(stream)))
 
 
 class VerifyAttention:

@@ -91,6 +91,15 @@ struct PartialArgs {
   float qk_scale_log2;  // sm_scale * log2(e)
 };
 
+struct AppendArgs {
+  const uint16_t* kv_new;
+  const int32_t* slot_idx;
+  const int32_t* seq_lens;
+  uint16_t* kv_pool;
+  int B, T, max_seq_len;
+  int64_t total_kv, pool_slots;
+};
+
 struct CombineArgs {
   const float* part_o;
   const float* part_ml;
@@ -736,6 +745,30 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
   *reinterpret_cast<u32x4*>(a.out + grow * V_DIM + 8 * lane) = packed;
 }
 
+// ------------------------------------------------------------ append kernel
+// Draft-row KV append: row (b, t) of kv_new -> kv_pool[slot of tree node t of
+// sequence b] (the last T entries of the sequence's slot_idx segment). One
+// wave per row: 64 lanes copy 1,024 bytes, lanes 0..7 the last 128.
+__global__ __launch_bounds__(256) void verify_attn_append_kernel(AppendArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // b * T + t
+  if (r >= (int64_t)a.B * a.T) return;
+  const int b = (int)(r / a.T);
+  const int t = (int)(r - (int64_t)b * a.T);
+  long long seg = 0;  // segment start: sum of the (clamped) lengths of sequences < b
+  for (int bb = lane; bb < b; bb += 64) seg += clamp_len(a.seq_lens[bb], a.T, a.max_seq_len);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) seg += __shfl_xor(seg, d);
+  int64_t si = seg + clamp_len(a.seq_lens[b], a.T, a.max_seq_len) - a.T + t;
+  si = si < a.total_kv - 1 ? si : a.total_kv - 1;
+  const int slot = a.slot_idx[si];
+  if (slot < 0 || (int64_t)slot >= a.pool_slots) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(a.kv_new + r * KV_DIM);
+  u32x4* dst = reinterpret_cast<u32x4*>(a.kv_pool + (int64_t)slot * KV_DIM);
+  dst[lane] = src[lane];
+  if (lane < 8) dst[64 + lane] = src[64 + lane];
+}
+
 // ------------------------------------------------------------------- host
 
 constexpr int NUM_CUS = 256;        // MI355X compute units (one partial workgroup each)
@@ -952,6 +985,30 @@ int verify_attn(const verify_attn_params* p, const void* q, const void* kv_pool,
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if ((rc = launch_partial(p, pl, q, kv_pool, slot_idx, seq_lens, tree_parent, workspace, s))) return rc;
   return launch_combine(p, pl, seq_lens, out, workspace, s);
+}
+
+int verify_attn_append_kv(const verify_attn_params* p, const void* kv_new, const int32_t* slot_idx,
+                          const int32_t* seq_lens, void* kv_pool, void* stream) {
+  int rc = validate(p);
+  if (rc) return rc;
+  if (!kv_new || !slot_idx || !seq_lens || !kv_pool) return VERIFY_ATTN_ERR_NULL_PTR;
+  if (!aligned16(kv_new) || !aligned16(kv_pool)) return VERIFY_ATTN_ERR_MISALIGNED;
+  if ((rc = check_device())) return rc;
+  AppendArgs a;
+  a.kv_new = static_cast<const uint16_t*>(kv_new);
+  a.slot_idx = slot_idx;
+  a.seq_lens = seq_lens;
+  a.kv_pool = static_cast<uint16_t*>(kv_pool);
+  a.B = p->num_seqs;
+  a.T = p->tree_size;
+  a.max_seq_len = p->max_seq_len;
+  a.total_kv = p->total_kv;
+  a.pool_slots = p->pool_slots;
+  const int64_t rows = (int64_t)a.B * a.T;
+  if (ceil_div64(rows, 4) > INT32_MAX) return VERIFY_ATTN_ERR_BAD_DIM;
+  hipLaunchKernelGGL(verify_attn_append_kernel, dim3((unsigned)ceil_div64(rows, 4)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? VERIFY_ATTN_OK : VERIFY_ATTN_ERR_LAUNCH_FAILED;
 }
 
 const char* verify_attn_strerror(int status) {

@@ -12,6 +12,8 @@ Parity status of each oracle function (pins live in tests/test_oracle_pins.py):
       an explicit mask, closed forms, invariants, planted-mistake checks).
   oracle_row_weights: pinned (weights sum to 1, zero outside the visible set,
       match the library routine's attention probabilities).
+  append_kv (NumPy, below): pinned (re-appending a workload's own tree rows
+      into a pool where they were cleared restores the pool exactly).
 """
 from __future__ import annotations
 
@@ -132,6 +134,27 @@ class Oracle:
 
 
 _default: Optional[Oracle] = None
+
+
+def append_kv(kv_pool: np.ndarray, kv_new: np.ndarray, slot_idx: np.ndarray,
+              seq_lens: np.ndarray) -> np.ndarray:
+    """Draft-row KV append, written out: returns a copy of kv_pool ([slots, 576]
+    bf16 bits) with row (b, t) of kv_new ([B, T, 576]) stored at the slot of
+    tree node t of sequence b, slot_idx[seg_b + seq_lens[b] - T + t], where
+    seg_b is the sum of the earlier sequences' lengths (the extend layout: a
+    sequence's prefix slots, then its draft tokens' slots in node order).
+    Slots outside the pool are skipped."""
+    out = np.array(kv_pool, copy=True)
+    B, T, _ = kv_new.shape
+    seg = 0
+    for b in range(B):
+        n = int(seq_lens[b])
+        for t in range(T):
+            slot = int(slot_idx[seg + n - T + t])
+            if 0 <= slot < out.shape[0]:
+                out[slot] = kv_new[b, t]
+        seg += n
+    return out
 
 
 def load(path: Optional[str] = None) -> Oracle:

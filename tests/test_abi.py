@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert mtv.verify_attn_version() == (1 << 16)
+    assert mtv.verify_attn_version() == (1 << 16) | 1
 
 
 def base_params(**kw):
@@ -124,3 +124,25 @@ def test_no_device_here(lib):
 def test_strerror_total(lib):
     for code in range(-12, 2):
         assert isinstance(mtv.verify_attn_strerror(code), str)
+
+
+def test_append_kv_errors(lib):
+    """The draft-row append validates like the verify call and checks its own
+    pointers before touching a device."""
+    p = base_params()
+    a = 1 << 20
+    args = [a, a, a, a]  # kv_new, slot_idx, seq_lens, kv_pool
+    for i in range(4):
+        bad = list(args)
+        bad[i] = None
+        assert lib.verify_attn_append_kv(ctypes.byref(p), *bad, None) == header_enum("VERIFY_ATTN_ERR_NULL_PTR"), i
+    for i in (0, 3):  # kv_new and kv_pool must be 16-byte aligned
+        bad = list(args)
+        bad[i] = a + 8
+        assert lib.verify_attn_append_kv(ctypes.byref(p), *bad, None) == header_enum("VERIFY_ATTN_ERR_MISALIGNED"), i
+    q = base_params(tree_size=0)
+    assert lib.verify_attn_append_kv(ctypes.byref(q), *args, None) == header_enum("VERIFY_ATTN_ERR_TREE_TOO_LARGE")
+    assert lib.verify_attn_append_kv(None, *args, None) == header_enum("VERIFY_ATTN_ERR_NULL_PTR")
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert lib.verify_attn_append_kv(ctypes.byref(p), *args, None) == header_enum("VERIFY_ATTN_ERR_DEVICE")
