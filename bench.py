@@ -92,6 +92,7 @@ class Bench:
             self.reps.append(d)
         self.out = torch.empty((wl.B, wl.T, wl.H, 512), dtype=torch.bfloat16, device="cuda")
         self.kv_new = torch.zeros((wl.B, wl.T, 576), dtype=torch.bfloat16, device="cuda")
+        self.kv_dst = None
         torch.cuda.synchronize()
 
     def call(self, r, stage="full"):
@@ -107,6 +108,11 @@ class Bench:
         elif stage == "append":  # draft-row KV append (writes the tree rows of the pool)
             self.mtv.verify_attn_append_kv(self.kv_new, d["slot_idx"], d["seq_lens"], d["kv_pool"],
                                            self.params)
+        elif stage == "compact":  # KV defragmentation: every referenced row into one contiguous run
+            if self.kv_dst is None:
+                self.kv_dst = self.torch.empty((self.wl.total_kv, 576), dtype=self.torch.bfloat16,
+                                               device="cuda")
+            self.mtv.verify_attn_compact_kv(d["kv_pool"], d["slot_idx"], self.kv_dst, self.params)
 
     def graph(self, n, stage):
         torch = self.torch
@@ -249,10 +255,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4a_long_scattered")
-    ap.add_argument("--extras", default="e1_h64_65k,c5_ragged,c4b_long_contiguous,e2_h8_t9_65k",
+    ap.add_argument("--extras", default="c4b_long_contiguous,e2_h8_t9_65k,e1_h64_65k,c5_ragged",
                     help="comma-separated extra workloads reported beside the headline ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stage", default=None, choices=[None, "full", "partial", "combine", "copy"],
+    ap.add_argument("--stage", default=None, choices=[None, "full", "partial", "combine", "append", "compact", "copy"],
                     help="profiling aid: only run K calls of one stage of the headline workload; "
                          "'copy' runs K device-to-device copies of 1 GiB (counter calibration)")
     ap.add_argument("--summarize", action="store_true",
@@ -301,7 +307,7 @@ def main():
         print(json.dumps({"stage": args.stage, "workload": args.workload, "calls": args.warmup + args.steps}))
         return
 
-    head = measure(args.workload, args.steps, args.warmup, stages=("full", "partial", "append"))
+    head = measure(args.workload, args.steps, args.warmup, stages=("full", "partial", "append", "compact"))
     ms = head["full_ms"]
     gbs = head["bytes"] / (ms * 1e-3) / 1e9
     part_ms = head["partial_ms"]
@@ -362,6 +368,12 @@ def main():
             "rows": head["wl"].B * head["wl"].T,
             "us_per_call": round(head["append_ms"] * 1e3, 2),
             "gbs": round(2 * KV_ROW_BYTES * head["wl"].B * head["wl"].T / (head["append_ms"] * 1e-3) / 1e9, 1),
+        },
+        # KV defragmentation on the same workload: total_kv rows of 1,152 B gathered and written
+        "compact_kv": {
+            "rows": head["wl"].total_kv,
+            "us_per_call": round(head["compact_ms"] * 1e3, 2),
+            "gbs": round(2 * KV_ROW_BYTES * head["wl"].total_kv / (head["compact_ms"] * 1e-3) / 1e9, 1),
         },
     }
     if not args.no_cpu_baseline:

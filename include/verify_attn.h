@@ -167,13 +167,30 @@ int verify_attn_plan(const verify_attn_params* p, verify_attn_plan_info* info);
 int verify_attn_append_kv(const verify_attn_params* p, const void* kv_new, const int32_t* slot_idx,
                           const int32_t* seq_lens, void* kv_pool, void* stream);
 
+/*
+ * KV defragmentation: copy every referenced latent row into consecutive rows,
+ *   kv_dst[i] = kv_pool[slot_idx[i]]   for i < total_kv,
+ * i.e. each sequence's KV (prefix rows, then its tree nodes' rows) becomes one
+ * contiguous run of rows, as the pages' planned defragmentation phase keeps a
+ * request's KV contiguous ("The Checkpoint Report", Architecture of the Report and Input
+ * Knowledge). A verify_attn call on kv_dst with slot_idx[i] = i (page_size 64)
+ * then gives the same result bit for bit. Uses total_kv and pool_slots of `p`.
+ *   kv_pool  bf16 [pool_slots, 576], 16-byte aligned (read)
+ *   slot_idx int32 [total_kv] (read)
+ *   kv_dst   bf16 [total_kv, 576], 16-byte aligned, must not overlap kv_pool (written)
+ * Enqueued on `stream`; no allocation, no host synchronisation. A slot outside
+ * [0, pool_slots) yields a row of zeros. Status codes as above.
+ */
+int verify_attn_compact_kv(const verify_attn_params* p, const void* kv_pool, const int32_t* slot_idx,
+                           void* kv_dst, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* verify_attn_strerror(int status);
 
-/* ABI version of this header: (major << 16) | minor (minor 1: verify_attn_append_kv). */
+/* ABI version of this header: (major << 16) | minor (minor 1: verify_attn_append_kv; 2: verify_attn_compact_kv). */
 int verify_attn_version(void);
 
-#define VERIFY_ATTN_VERSION ((1 << 16) | 1)
+#define VERIFY_ATTN_VERSION ((1 << 16) | 2)
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,7 @@ raise.
 
 Entry points mirror the C ABI declared in ``include/verify_attn.h``:
 ``verify_attn``, ``verify_attn_partial``, ``verify_attn_combine``,
-``verify_attn_append_kv``, ``verify_attn_workspace_size``, ``verify_attn_plan``,
+``verify_attn_append_kv``, ``verify_attn_compact_kv``, ``verify_attn_workspace_size``, ``verify_attn_plan``,
 ``verify_attn_strerror``, ``verify_attn_version``.
 """
 from __future__ import annotations
@@ -26,6 +26,7 @@ MAX_TREE = 64
 
 EXPORTS = (
     "verify_attn", "verify_attn_partial", "verify_attn_combine", "verify_attn_append_kv",
+    "verify_attn_compact_kv",
     "verify_attn_workspace_size",
     "verify_attn_plan", "verify_attn_strerror", "verify_attn_version",
 )
@@ -81,6 +82,8 @@ def load_library(path: str = LIB_PATH):
     lib.verify_attn_combine.restype = ctypes.c_int
     lib.verify_attn_append_kv.argtypes = [P, vp, i32p, i32p, vp, vp]
     lib.verify_attn_append_kv.restype = ctypes.c_int
+    lib.verify_attn_compact_kv.argtypes = [P, vp, i32p, vp, vp]
+    lib.verify_attn_compact_kv.restype = ctypes.c_int
     lib.verify_attn_plan.argtypes = [P, ctypes.POINTER(PlanInfo)]
     lib.verify_attn_plan.restype = ctypes.c_int
     lib.verify_attn_strerror.argtypes = [ctypes.c_int]
@@ -213,6 +216,20 @@ def verify_attn_append_kv(kv_new, slot_idx, seq_lens, kv_pool, params: Params, s
     _check(load_library().verify_attn_append_kv(
         ctypes.byref(params), _ptr(kv_new), _ptr(slot_idx), _ptr(seq_lens), _ptr(kv_pool),
         _stream(stream)))
+
+
+def verify_attn_compact_kv(kv_pool, slot_idx, kv_dst, params: Params, stream=None) -> None:
+    """Enqueue the KV defragmentation: kv_dst[i] = kv_pool[slot_idx[i]]."""
+    import torch
+    for name, t in dict(kv_pool=kv_pool, slot_idx=slot_idx, kv_dst=kv_dst).items():
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if kv_pool.dtype != torch.bfloat16 or kv_dst.dtype != torch.bfloat16 or slot_idx.dtype != torch.int32:
+        raise ValueError("kv_pool / kv_dst must be bfloat16, slot_idx int32")
+    if tuple(kv_dst.shape) != (int(params.total_kv), KV_DIM) or kv_pool.dim() != 2 or kv_pool.shape[1] != KV_DIM:
+        raise ValueError("kv_dst must be [total_kv, 576] and kv_pool [slots, 576]")
+    _check(load_library().verify_attn_compact_kv(
+        ctypes.byref(params), _ptr(kv_pool), _ptr(slot_idx), _ptr(kv_dst), _stream(stream)))
 
 
 class VerifyAttention:

@@ -100,6 +100,13 @@ struct AppendArgs {
   int64_t total_kv, pool_slots;
 };
 
+struct CompactArgs {
+  const uint16_t* kv_pool;
+  const int32_t* slot_idx;
+  uint16_t* kv_dst;
+  int64_t total_kv, pool_slots;
+};
+
 struct CombineArgs {
   const float* part_o;
   const float* part_ml;
@@ -769,6 +776,28 @@ __global__ __launch_bounds__(256) void verify_attn_append_kernel(AppendArgs a) {
   if (lane < 8) dst[64 + lane] = src[64 + lane];
 }
 
+// ------------------------------------------------------------ compact kernel
+// KV defragmentation: kv_dst[i] = kv_pool[slot_idx[i]]. One wave per row, four
+// rows per workgroup; 16 bytes per lane (the last 128 bytes on lanes 0..7).
+__global__ __launch_bounds__(256) void verify_attn_compact_kernel(CompactArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= a.total_kv) return;
+  const int slot = a.slot_idx[i];
+  u32x4* dst = reinterpret_cast<u32x4*>(a.kv_dst + i * KV_DIM);
+  if (slot < 0 || (int64_t)slot >= a.pool_slots) {
+    dst[lane] = u32x4{0u, 0u, 0u, 0u};
+    if (lane < 8) dst[64 + lane] = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+  const u32x4* src = reinterpret_cast<const u32x4*>(a.kv_pool + (int64_t)slot * KV_DIM);
+  const u32x4 v0 = src[lane];
+  u32x4 v1 = {0u, 0u, 0u, 0u};
+  if (lane < 8) v1 = src[64 + lane];
+  dst[lane] = v0;
+  if (lane < 8) dst[64 + lane] = v1;
+}
+
 // ------------------------------------------------------------------- host
 
 constexpr int NUM_CUS = 256;        // MI355X compute units (one partial workgroup each)
@@ -1007,6 +1036,25 @@ int verify_attn_append_kv(const verify_attn_params* p, const void* kv_new, const
   const int64_t rows = (int64_t)a.B * a.T;
   if (ceil_div64(rows, 4) > INT32_MAX) return VERIFY_ATTN_ERR_BAD_DIM;
   hipLaunchKernelGGL(verify_attn_append_kernel, dim3((unsigned)ceil_div64(rows, 4)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? VERIFY_ATTN_OK : VERIFY_ATTN_ERR_LAUNCH_FAILED;
+}
+
+int verify_attn_compact_kv(const verify_attn_params* p, const void* kv_pool, const int32_t* slot_idx,
+                           void* kv_dst, void* stream) {
+  int rc = validate(p);
+  if (rc) return rc;
+  if (!kv_pool || !slot_idx || !kv_dst) return VERIFY_ATTN_ERR_NULL_PTR;
+  if (!aligned16(kv_pool) || !aligned16(kv_dst)) return VERIFY_ATTN_ERR_MISALIGNED;
+  if ((rc = check_device())) return rc;
+  CompactArgs a;
+  a.kv_pool = static_cast<const uint16_t*>(kv_pool);
+  a.slot_idx = slot_idx;
+  a.kv_dst = static_cast<uint16_t*>(kv_dst);
+  a.total_kv = p->total_kv;
+  a.pool_slots = p->pool_slots;
+  if (ceil_div64(a.total_kv, 4) > INT32_MAX) return VERIFY_ATTN_ERR_BAD_DIM;
+  hipLaunchKernelGGL(verify_attn_compact_kernel, dim3((unsigned)ceil_div64(a.total_kv, 4)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? VERIFY_ATTN_OK : VERIFY_ATTN_ERR_LAUNCH_FAILED;
 }

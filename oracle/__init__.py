@@ -14,6 +14,8 @@ Parity status of each oracle function (pins live in tests/test_oracle_pins.py):
       match the library routine's attention probabilities).
   append_kv (NumPy, below): pinned (re-appending a workload's own tree rows
       into a pool where they were cleared restores the pool exactly).
+  compact_kv (NumPy, below): pinned (compacting the scattered long-context
+      workload reproduces the generator's defragmented pool rows).
 """
 from __future__ import annotations
 
@@ -154,6 +156,16 @@ def append_kv(kv_pool: np.ndarray, kv_new: np.ndarray, slot_idx: np.ndarray,
             if 0 <= slot < out.shape[0]:
                 out[slot] = kv_new[b, t]
         seg += n
+    return out
+
+
+def compact_kv(kv_pool: np.ndarray, slot_idx: np.ndarray) -> np.ndarray:
+    """KV defragmentation, written out: row i of the result is pool row
+    slot_idx[i] (a row of zeros for a slot outside the pool)."""
+    out = np.zeros((slot_idx.shape[0], kv_pool.shape[1]), dtype=kv_pool.dtype)
+    for i, slot in enumerate(slot_idx.tolist()):
+        if 0 <= slot < kv_pool.shape[0]:
+            out[i] = kv_pool[slot]
     return out
 
 

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert mtv.verify_attn_version() == (1 << 16) | 1
+    assert mtv.verify_attn_version() == (1 << 16) | 2
 
 
 def base_params(**kw):
@@ -146,3 +146,25 @@ def test_append_kv_errors(lib):
     import torch
     if torch.cuda.device_count() == 0:
         assert lib.verify_attn_append_kv(ctypes.byref(p), *args, None) == header_enum("VERIFY_ATTN_ERR_DEVICE")
+
+
+def test_compact_kv_errors(lib):
+    """The KV compaction validates like the verify call and checks its own
+    pointers before touching a device."""
+    p = base_params()
+    a = 1 << 20
+    args = [a, a, a]  # kv_pool, slot_idx, kv_dst
+    for i in range(3):
+        bad = list(args)
+        bad[i] = None
+        assert lib.verify_attn_compact_kv(ctypes.byref(p), *bad, None) == header_enum("VERIFY_ATTN_ERR_NULL_PTR"), i
+    for i in (0, 2):  # kv_pool and kv_dst must be 16-byte aligned
+        bad = list(args)
+        bad[i] = a + 8
+        assert lib.verify_attn_compact_kv(ctypes.byref(p), *bad, None) == header_enum("VERIFY_ATTN_ERR_MISALIGNED"), i
+    q = base_params(total_kv=0)
+    assert lib.verify_attn_compact_kv(ctypes.byref(q), *args, None) != 0
+    assert lib.verify_attn_compact_kv(None, *args, None) == header_enum("VERIFY_ATTN_ERR_NULL_PTR")
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert lib.verify_attn_compact_kv(ctypes.byref(p), *args, None) == header_enum("VERIFY_ATTN_ERR_DEVICE")
