@@ -56,10 +56,16 @@ constexpr float LAZY_RESCALE_LOG2 = 8.0f;  // running max is raised only past +8
 constexpr int QK_AHEAD = 4;                // K operand reads in flight ahead of their MFMA
 constexpr int PV_AHEAD = 4;                // V^T operand reads in flight ahead
 constexpr int SM_PIECES = 16;              // softmax pieces interleaved with the next QK
+constexpr int COMBINE_BATCH = 8;           // partials per batch of loads in the combine kernel
+#ifndef VERIFY_ATTN_Q_EARLY
+#define VERIFY_ATTN_Q_EARLY 12
+#endif
+constexpr int Q_EARLY = VERIFY_ATTN_Q_EARLY;  // query fragments loaded before the first gathers
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -71,7 +77,7 @@ struct Plan {
   int chunk;           // keys per split (multiple of NK)
   int max_splits;      // bound on the total number of splits
   int partial_blocks;  // multiple of 8
-  int combine_wpr;     // waves per output row in the combine kernel (1, 4 or 16)
+  int combine_wpr;     // waves per output row in the combine kernel (1, 2, 4, 8 or 16)
   int combine_blocks;
   size_t part_o_bytes;
   size_t ws_bytes;
@@ -186,6 +192,62 @@ __device__ int count_splits(const int32_t* __restrict__ seq_lens, int B, int T, 
     total += ns;
   }
   return total;
+}
+
+// Work item of a partial-kernel workgroup. Items are (split, row tile) pairs
+// over the splits of all sequences; workgroup ids are dealt to the 8 XCDs
+// round-robin, so each XCD gets a contiguous, equal share of the items that
+// exist for these sequence lengths (the row tiles of one split then share that
+// XCD's L2 for their KV reads). For B <= 64 one load of seq_lens serves both
+// the item count and the split's location; larger batches scan twice.
+__device__ bool locate_item(const int32_t* __restrict__ seq_lens, int B, int T, int max_len, int chunk,
+                            int max_splits, int row_tiles, int* g_out, int* rt_out, SplitLoc* loc) {
+  const int lane = threadIdx.x & 63;
+  if (B > 64) {
+    int n_items = count_splits(seq_lens, B, T, max_len, chunk);
+    n_items = __builtin_amdgcn_readfirstlane(min(n_items, max_splits) * row_tiles);
+    const int per_xcd = (n_items + 7) >> 3;
+    const int k_on_xcd = blockIdx.x >> 3;
+    const int logical = (blockIdx.x & 7) * per_xcd + k_on_xcd;
+    if (k_on_xcd >= per_xcd || logical >= n_items) return false;
+    *g_out = logical / row_tiles;
+    *rt_out = logical - *g_out * row_tiles;
+    return locate_split(seq_lens, B, T, max_len, chunk, *g_out, false, loc);
+  }
+  int len = 0, ns = 0;
+  if (lane < B) {
+    len = clamp_len(seq_lens[lane], T, max_len);
+    ns = (len + chunk - 1) / chunk;
+  }
+  int ns_inc = ns;
+  long long len_inc = len;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int x = __shfl_up(ns_inc, d);
+    const long long y = __shfl_up(len_inc, d);
+    if (lane >= d) {
+      ns_inc += x;
+      len_inc += y;
+    }
+  }
+  const int n_items = __builtin_amdgcn_readfirstlane(min(__shfl(ns_inc, 63), max_splits) * row_tiles);
+  const int per_xcd = (n_items + 7) >> 3;
+  const int k_on_xcd = blockIdx.x >> 3;
+  const int logical = (blockIdx.x & 7) * per_xcd + k_on_xcd;
+  if (k_on_xcd >= per_xcd || logical >= n_items) return false;
+  const int g = logical / row_tiles;
+  const int ns_first = ns_inc - ns;
+  const unsigned long long mask = __ballot(lane < B && g >= ns_first && g < ns_first + ns);
+  if (!mask) return false;
+  const int src = __ffsll((long long)mask) - 1;
+  loc->b = __shfl(lane, src);
+  loc->g0 = __shfl(ns_first, src);
+  loc->n_splits = __shfl(ns, src);
+  loc->len = __shfl(len, src);
+  loc->seg = __shfl(len_inc - len, src);
+  *g_out = g;
+  *rt_out = logical - g * row_tiles;
+  return true;
 }
 
 // Swizzle of the 16-byte chunk position inside a 128-byte row segment:
@@ -346,22 +408,11 @@ void verify_attn_partial_kernel(PartialArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // XCD-aware order: workgroup ids are dealt to the 8 XCDs round-robin, so give
-  // each XCD a contiguous, equal share of the (split, row tile) work items that
-  // exist for these sequence lengths; the row tiles of one split then share that
-  // XCD's L2 for their KV reads, and no XCD gets more items than another.
-  int n_items = count_splits(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk);
-  n_items = __builtin_amdgcn_readfirstlane(min(n_items, a.max_splits) * a.row_tiles);
-  const int per_xcd = (n_items + 7) >> 3;
-  const int k_on_xcd = blockIdx.x >> 3;
-  if (k_on_xcd >= per_xcd) return;
-  const int logical = (blockIdx.x & 7) * per_xcd + k_on_xcd;
-  if (logical >= n_items) return;
-  const int g = logical / a.row_tiles;
-  const int rt = logical - g * a.row_tiles;
-
+  int g, rt;
   SplitLoc loc;
-  if (!locate_split(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, g, false, &loc)) return;
+  if (!locate_item(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, a.max_splits, a.row_tiles, &g, &rt, &loc)) return;
+  g = __builtin_amdgcn_readfirstlane(g);
+  rt = __builtin_amdgcn_readfirstlane(rt);
   loc.b = __builtin_amdgcn_readfirstlane(loc.b);
   loc.g0 = __builtin_amdgcn_readfirstlane(loc.g0);
   loc.len = __builtin_amdgcn_readfirstlane(loc.len);
@@ -403,15 +454,16 @@ void verify_attn_partial_kernel(PartialArgs a) {
     return smem_base + (t % NBUF) * TILE_BYTES + wave * (ROWS_PER_LOAD_WAVE * 128);
   };
 
-  // Prologue loads, oldest first: the slot entries of tiles 0 and 1 (lane: row
-  // lane/8 of this wave's 8), the tree's parent pointers (wave 0), the query
-  // fragments. The gathers of tiles 0 and 1 start as soon as the slot entries
-  // are in, while the query loads are still on their way.
+  // Prologue loads, oldest first: the tree's parent pointers (wave 0) and the
+  // slot entries of tiles 0 and 1 (lane: row lane/8 of this wave's 8), the
+  // first Q_EARLY query fragments; then, once the slot entries are in, the
+  // gathers of tiles 0 and 1, and the remaining query fragments behind them,
+  // so that the query streams in while the first KV rows are on their way.
+  int parent = -1;
+  if (wave == 0 && lane < a.T) parent = a.tree_parent[(int64_t)loc.b * a.T + lane];
   int s_pro[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) s_pro[t] = *slot_ptr(k0 + t * NK, lane >> 3);
-  int parent = -1;
-  if (wave == 0 && lane < a.T) parent = a.tree_parent[(int64_t)loc.b * a.T + lane];
   // Query fragments (B operand of S^T = K Q^T): lane l holds row l%32,
   // features 16 ks + 8 (l/32) .. +7 of k-step ks. Waves without query rows
   // run the same schedule on zeros (they still gather their share of the KV).
@@ -421,28 +473,33 @@ void verify_attn_partial_kernel(PartialArgs a) {
   const bool row_ok = qrow < a.M;
   const int hl = lane >> 5;  // lane half
   bf16x8 qf[QK_STEPS];
-  {
-    const uint16_t* src = a.q + ((int64_t)loc.b * a.M + (row_ok ? qrow : 0)) * KV_DIM + 8 * hl;
+  const uint16_t* qsrc = a.q + ((int64_t)loc.b * a.M + (row_ok ? qrow : 0)) * KV_DIM + 8 * hl;
+  // Unconditional loads (rows past M read row 0, which exists), then a
+  // select: no branches, so the waits for the slot entries stay exact.
+  auto load_q = [&](int ks) {
+    u32x4 v = *reinterpret_cast<const u32x4*>(qsrc + 16 * ks);
+    if (!row_ok) v = u32x4{0u, 0u, 0u, 0u};
+    qf[ks] = __builtin_bit_cast(bf16x8, v);
+  };
 #pragma unroll
-    for (int ks = 0; ks < QK_STEPS; ++ks) {
-      // Unconditional load (rows past M read row 0, which exists), then a
-      // select: no branches, so the waits for the slot entries stay exact.
-      u32x4 v = *reinterpret_cast<const u32x4*>(src + 16 * ks);
-      if (!row_ok) v = u32x4{0u, 0u, 0u, 0u};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
+  for (int ks = 0; ks < Q_EARLY; ++ks) load_q(ks);
 
   // Steady-state load order (iteration i: slots of tile i+5, gather of tile
-  // i+3) for i = -3, -2: the gathers of tiles 0 and 1.
+  // i+3) for i = -3, -2: the gathers of tiles 0 and 1. Both row addresses are
+  // formed before the first of these loads goes out, so the one wait for the
+  // slot entries comes before them and does not cover the gather of tile 0.
+  const uint16_t* src_pro[2] = {gather_src(s_pro[0]), gather_src(s_pro[1])};
+  asm volatile("" ::"v"(src_pro[0]), "v"(src_pro[1]));
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     issue_slots(t + 2);
-    const uint16_t* src = gather_src(s_pro[t]);
+    const uint16_t* src = src_pro[t];
     const uint32_t dst = gather_dst(t);
 #pragma unroll
     for (int j = 0; j < CHUNK_GROUPS; ++j) load_to_lds16(src + 64 * j, dst + j * GROUP_BYTES);
   }
+#pragma unroll
+  for (int ks = Q_EARLY; ks < QK_STEPS; ++ks) load_q(ks);
 
   // Ancestor masks of this sequence's tree (bit u of anc[t]: node u is t or an
   // ancestor of t), by pointer jumping over the lanes of wave 0: after round k
@@ -622,9 +679,10 @@ void verify_attn_partial_kernel(PartialArgs a) {
     }
   };
 
-  // Tile 0: publish it (own loads of tile 0 and the slots of tile 2 landed),
-  // then its QK (carrying the gather of tile 2).
-  wait_vmcnt<CHUNK_GROUPS + 1>();
+  // Tile 0: publish it (own loads of tile 0 and the slots of tile 2 landed;
+  // younger: the slots of tile 3, the gather of tile 1 and the late query
+  // fragments), then its QK (carrying the gather of tile 2).
+  wait_vmcnt<CHUNK_GROUPS + 1 + (QK_STEPS - Q_EARLY)>();
   lds_barrier();  // tile 0 complete; ancestor masks visible
   sv = qk_tile(0, false);
   // Iteration it: QK of tile it+1 with the softmax of tile it in between, then
@@ -681,11 +739,16 @@ void verify_attn_partial_kernel(PartialArgs a) {
 // sequence's splits s, M = max_s m_s, rounded to bf16 (nearest even).
 // WPR waves share one row: wave k reduces splits k, k + WPR, ... in order, and
 // the WPR wave results are merged in wave order through LDS, so the result
-// does not depend on timing. Lane j covers features 8j .. 8j+7.
+// does not depend on timing. Lane j covers features 4j .. 4j+3 and
+// 256 + 4j .. +3, so each load instruction reads 1 KB of one partial row. A
+// wave takes its splits COMBINE_BATCH at a time with every load of the batch
+// issued before the first use (one memory round trip per batch), keeping a
+// running maximum and rescaling its sums when the maximum rises.
 template <int WPR>
 __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_kernel(CombineArgs a) {
   constexpr int WAVES = WPR < 4 ? 4 : WPR;
   constexpr int ROWS = WAVES / WPR;
+  constexpr int BATCH = COMBINE_BATCH;
   __shared__ float red_ml[WAVES][2];
   __shared__ f32x4 red_o[WPR > 1 ? WAVES : 1][2 * 64];
 
@@ -704,20 +767,45 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
   int g_end = loc.g0 + loc.n_splits;
   g_end = g_end < a.max_splits ? g_end : a.max_splits;
 
-  float mloc = -INFINITY;
-  for (int g = loc.g0 + sub; g < g_end; g += WPR) mloc = fmaxf(mloc, a.part_ml[2 * ((int64_t)g * a.M + row)]);
-
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  float mloc = -INFINITY;  // running maximum of this wave's splits
   float L = 0.f;
-  for (int g = loc.g0 + sub; g < g_end; g += WPR) {
-    const int64_t rowid = (int64_t)g * a.M + row;
-    const float m = a.part_ml[2 * rowid];
-    const float l = a.part_ml[2 * rowid + 1];
-    const float w = (m == -INFINITY) ? 0.f : exp2f(m - mloc);
-    const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + rowid * V_DIM + 8 * lane);
-    acc0 += w * src[0];
-    acc1 += w * src[1];
-    L += w * l;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int base = loc.g0 + sub; base < g_end; base += WPR * BATCH) {
+    float m[BATCH], l[BATCH];
+    f32x4 o0[BATCH], o1[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      m[j] = -INFINITY;
+      l[j] = 0.f;
+      o0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      o1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (base + j * WPR < g_end) {  // wave-uniform
+        const int64_t rowid = (int64_t)(base + j * WPR) * a.M + row;
+        const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * rowid);
+        m[j] = ml[0];
+        l[j] = ml[1];
+        const float* src = a.part_o + rowid * V_DIM + 4 * lane;
+        o0[j] = *reinterpret_cast<const f32x4*>(src);
+        o1[j] = *reinterpret_cast<const f32x4*>(src + 256);
+      }
+    }
+    float mb = mloc;
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) mb = fmaxf(mb, m[j]);
+    if (mb > mloc) {  // the same for every lane (one row per wave)
+      const float s = exp2f(mloc - mb);  // mloc = -inf -> 0
+      acc0 *= s;
+      acc1 *= s;
+      L *= s;
+      mloc = mb;
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const float w = (m[j] != -INFINITY) ? exp2f(m[j] - mloc) : 0.f;
+      acc0 += w * o0[j];
+      acc1 += w * o1[j];
+      L += w * l[j];
+    }
   }
 
   if constexpr (WPR > 1) {
@@ -744,12 +832,15 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
   }
   if (!active) return;
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  u32x4 packed;
-  packed[0] = (uint32_t)f32_to_bf16_rne(acc0[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc0[1] * inv) << 16);
-  packed[1] = (uint32_t)f32_to_bf16_rne(acc0[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc0[3] * inv) << 16);
-  packed[2] = (uint32_t)f32_to_bf16_rne(acc1[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc1[1] * inv) << 16);
-  packed[3] = (uint32_t)f32_to_bf16_rne(acc1[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc1[3] * inv) << 16);
-  *reinterpret_cast<u32x4*>(a.out + grow * V_DIM + 8 * lane) = packed;
+  auto pack4 = [&](const f32x4& v) {
+    uint2 p;
+    p.x = (uint32_t)f32_to_bf16_rne(v[0] * inv) | ((uint32_t)f32_to_bf16_rne(v[1] * inv) << 16);
+    p.y = (uint32_t)f32_to_bf16_rne(v[2] * inv) | ((uint32_t)f32_to_bf16_rne(v[3] * inv) << 16);
+    return p;
+  };
+  uint16_t* dst = a.out + grow * V_DIM + 4 * lane;
+  *reinterpret_cast<uint2*>(dst) = pack4(acc0);
+  *reinterpret_cast<uint2*>(dst + 256) = pack4(acc1);
 }
 
 // ------------------------------------------------------------ append kernel
@@ -802,6 +893,7 @@ __global__ __launch_bounds__(256) void verify_attn_compact_kernel(CompactArgs a)
 
 constexpr int NUM_CUS = 256;        // MI355X compute units (one partial workgroup each)
 constexpr int MIN_CHUNK = 256;      // keys per split below which partials dominate
+constexpr int64_t COMBINE_WAVES = 4096;  // combine waves resident at once (16 per CU)
 
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -848,12 +940,14 @@ int make_plan(const verify_attn_params* p, Plan* pl) {
   if (chunk > len_cap) chunk = len_cap;
   const int64_t max_splits = ceil_div64(p->total_kv, chunk) + p->num_seqs;
   const int64_t blocks = ceil_div64(max_splits * row_tiles, 8) * 8;
-  // Combine: enough waves per row that the split partials are read with many
-  // loads in flight even when there are few rows.
+  // Combine: waves per row (a power of two up to 16, no more than the row's
+  // splits) so that all rows' waves fit in about one round of the chip
+  // (COMBINE_WAVES), each wave taking its splits in batches of COMBINE_BATCH.
   const int64_t rows = (int64_t)p->num_seqs * M;
   const int64_t seq_splits = ceil_div64(p->max_seq_len, chunk);
-  const int wpr = (seq_splits >= 16 && rows <= 2048) ? 16 : (seq_splits >= 4 ? 4 : 1);
-  const int64_t cblocks = wpr == 1 ? ceil_div64(rows, 4) : rows;
+  int wpr = 1;
+  while (wpr < 16 && rows * wpr * 2 <= COMBINE_WAVES && wpr * 2 <= seq_splits) wpr *= 2;
+  const int64_t cblocks = ceil_div64(rows, (wpr < 4 ? 4 : wpr) / wpr);
   if (blocks > INT32_MAX || cblocks > INT32_MAX || max_splits > INT32_MAX) return VERIFY_ATTN_ERR_BAD_DIM;
   pl->M = (int)M;
   pl->row_tiles = (int)row_tiles;
@@ -925,12 +1019,14 @@ int launch_combine(const verify_attn_params* p, const Plan& pl, const int32_t* s
   a.chunk = pl.chunk;
   a.max_splits = pl.max_splits;
   a.max_seq_len = p->max_seq_len;
-  if (pl.combine_wpr == 16)
-    hipLaunchKernelGGL(verify_attn_combine_kernel<16>, dim3(pl.combine_blocks), dim3(16 * 64), 0, stream, a);
-  else if (pl.combine_wpr == 4)
-    hipLaunchKernelGGL(verify_attn_combine_kernel<4>, dim3(pl.combine_blocks), dim3(4 * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL(verify_attn_combine_kernel<1>, dim3(pl.combine_blocks), dim3(4 * 64), 0, stream, a);
+  const dim3 grid(pl.combine_blocks);
+  switch (pl.combine_wpr) {
+    case 16: hipLaunchKernelGGL(verify_attn_combine_kernel<16>, grid, dim3(16 * 64), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(verify_attn_combine_kernel<8>, grid, dim3(8 * 64), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(verify_attn_combine_kernel<4>, grid, dim3(4 * 64), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(verify_attn_combine_kernel<2>, grid, dim3(4 * 64), 0, stream, a); break;
+    default: hipLaunchKernelGGL(verify_attn_combine_kernel<1>, grid, dim3(4 * 64), 0, stream, a); break;
+  }
   return hipGetLastError() == hipSuccess ? VERIFY_ATTN_OK : VERIFY_ATTN_ERR_LAUNCH_FAILED;
 }
 
