@@ -57,10 +57,10 @@ constexpr int QK_AHEAD = 4;                // K operand reads in flight ahead of
 constexpr int PV_AHEAD = 4;                // V^T operand reads in flight ahead
 constexpr int SM_PIECES = 16;              // softmax pieces interleaved with the next QK
 constexpr int COMBINE_BATCH = 8;           // partials per batch of loads in the combine kernel
-#ifndef VERIFY_ATTN_Q_EARLY
-#define VERIFY_ATTN_Q_EARLY 12
-#endif
-constexpr int Q_EARLY = VERIFY_ATTN_Q_EARLY;  // query fragments loaded before the first gathers
+constexpr int QSTAGE_PIECES = KV_DIM / 2 / 8;  // 36 16-byte pieces per row and half
+constexpr int QSTAGE_BYTES = ROWS_PER_WAVE * QSTAGE_PIECES * 16;  // 18 KB per wave
+constexpr int QSTAGE_LOADS = QSTAGE_BYTES / 1024;                 // 18 direct-to-LDS loads
+static_assert(NWAVES * QSTAGE_BYTES <= (NBUF - 2) * TILE_BYTES, "query staging fits tiles 2 and 3");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -399,7 +399,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // softmax requires. LDS buffers: tile it (PV), tile it+1 (QK), tiles it+2 and
 // it+3 in flight. One barrier per iteration publishes tile it+1 and, every
 // wave being done with iteration it-1, frees tile it-1's buffer for the gather
-// of tile it+3, whose nine loads ride on the QK MFMAs (one every four).
+// of tile it+3, whose nine loads ride on the first half of the QK MFMAs (one
+// every two), so the last of them has the rest of QK and all of PV to land.
 __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void verify_attn_partial_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * TILE_BYTES + SLOT_RING * NWAVES * 256];
@@ -455,39 +456,59 @@ void verify_attn_partial_kernel(PartialArgs a) {
   };
 
   // Prologue loads, oldest first: the tree's parent pointers (wave 0) and the
-  // slot entries of tiles 0 and 1 (lane: row lane/8 of this wave's 8), the
-  // first Q_EARLY query fragments; then, once the slot entries are in, the
-  // gathers of tiles 0 and 1, and the remaining query fragments behind them,
-  // so that the query streams in while the first KV rows are on their way.
+  // slot entries of tiles 0 and 1 (lane: row lane/8 of this wave's 8); the
+  // first half of this wave's query block into LDS; once the slot entries are
+  // in, the gathers of tiles 0 and 1; then the second half of the query block.
   int parent = -1;
   if (wave == 0 && lane < a.T) parent = a.tree_parent[(int64_t)loc.b * a.T + lane];
   int s_pro[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) s_pro[t] = *slot_ptr(k0 + t * NK, lane >> 3);
   // Query fragments (B operand of S^T = K Q^T): lane l holds row l%32,
-  // features 16 ks + 8 (l/32) .. +7 of k-step ks. Waves without query rows
-  // run the same schedule on zeros (they still gather their share of the KV).
+  // features 16 ks + 8 (l/32) .. +7 of k-step ks, i.e. 16-byte piece
+  // 2 ks + l/32 of its row. Waves without query rows run the same schedule on
+  // zeros (they still gather their share of the KV).
   const int row0 = rt * ROWS_PER_TILE + wave * ROWS_PER_WAVE;
   const bool wave_active = row0 < a.M;  // wave-uniform
   const int qrow = row0 + (lane & 31);
   const bool row_ok = qrow < a.M;
   const int hl = lane >> 5;  // lane half
   bf16x8 qf[QK_STEPS];
-  const uint16_t* qsrc = a.q + ((int64_t)loc.b * a.M + (row_ok ? qrow : 0)) * KV_DIM + 8 * hl;
-  // Unconditional loads (rows past M read row 0, which exists), then a
-  // select: no branches, so the waits for the slot entries stay exact.
-  auto load_q = [&](int ks) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(qsrc + 16 * ks);
-    if (!row_ok) v = u32x4{0u, 0u, 0u, 0u};
-    qf[ks] = __builtin_bit_cast(bf16x8, v);
-  };
+  // The query block passes through LDS in two halves (pieces 0..35 and
+  // 36..71 of each of the wave's 32 rows), in a region of the ring buffers of
+  // tiles 2 and 3, which are free until the QK of tile 0. Read straight into
+  // the MFMA layout, each load instruction would touch 32 rows; staged, each
+  // direct-to-LDS load reads 1 KB of consecutive query bytes. Staging slot
+  // s = 36 r + p' holds piece p' ^ ((r >> 1) & 3) of row r (a permutation
+  // inside aligned groups of four pieces), so that the MFMA-layout reads of
+  // eight consecutive rows fall on eight distinct 16-byte positions.
+  const uint32_t qstage = smem_base + 2 * TILE_BYTES + wave * QSTAGE_BYTES;
+  auto q_stage = [&](int half) {
 #pragma unroll
-  for (int ks = 0; ks < Q_EARLY; ++ks) load_q(ks);
+    for (int j = 0; j < QSTAGE_LOADS; ++j) {
+      const int slot = j * 64 + lane;
+      const int r = slot / QSTAGE_PIECES;
+      const int p = (slot - r * QSTAGE_PIECES) ^ ((r >> 1) & 3);
+      const int grow = row0 + r < a.M ? row0 + r : 0;  // rows past M read row 0
+      load_to_lds16(a.q + ((int64_t)loc.b * a.M + grow) * KV_DIM + half * (KV_DIM / 2) + 8 * p,
+                    qstage + j * 1024);
+    }
+  };
+  auto q_read = [&](int half) {
+    const int r = lane & 31;
+#pragma unroll
+    for (int k = 0; k < QK_STEPS / 2; ++k) {
+      const int p = 2 * k + hl;
+      u32x4 v = __builtin_bit_cast(u32x4, lds_read_b128(qstage + (r * QSTAGE_PIECES + (p ^ ((r >> 1) & 3))) * 16));
+      if (!row_ok) v = u32x4{0u, 0u, 0u, 0u};
+      qf[half * (QK_STEPS / 2) + k] = __builtin_bit_cast(bf16x8, v);
+    }
+  };
+  q_stage(0);
 
   // Steady-state load order (iteration i: slots of tile i+5, gather of tile
-  // i+3) for i = -3, -2: the gathers of tiles 0 and 1. Both row addresses are
-  // formed before the first of these loads goes out, so the one wait for the
-  // slot entries comes before them and does not cover the gather of tile 0.
+  // i+3) for i = -3, -2: the gathers of tiles 0 and 1. Forming their row
+  // addresses waits for the slot entries (and the first query half).
   const uint16_t* src_pro[2] = {gather_src(s_pro[0]), gather_src(s_pro[1])};
   asm volatile("" ::"v"(src_pro[0]), "v"(src_pro[1]));
 #pragma unroll
@@ -498,8 +519,15 @@ void verify_attn_partial_kernel(PartialArgs a) {
 #pragma unroll
     for (int j = 0; j < CHUNK_GROUPS; ++j) load_to_lds16(src + 64 * j, dst + j * GROUP_BYTES);
   }
-#pragma unroll
-  for (int ks = Q_EARLY; ks < QK_STEPS; ++ks) load_q(ks);
+  wait_vmcnt<2 * (CHUNK_GROUPS + 1)>();  // first query half in LDS (the gathers may still fly)
+  asm volatile("" ::: "memory");
+  q_read(0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 7, 0));  // read out before the second half lands
+  asm volatile("" ::: "memory");
+  q_stage(1);
+  wait_vmcnt<0>();  // second query half, and with it tiles 0 and 1, landed
+  asm volatile("" ::: "memory");
+  q_read(1);
 
   // Ancestor masks of this sequence's tree (bit u of anc[t]: node u is t or an
   // ancestor of t), by pointer jumping over the lanes of wave 0: after round k
@@ -617,8 +645,9 @@ void verify_attn_partial_kernel(PartialArgs a) {
   };
 
   // ---- S^T = K Q^T for tile t: 36 MFMAs, with the nine gather loads of tile
-  // t+2 (one every 4 MFMAs) and, when `with_softmax`, the softmax pieces of
-  // the previous tile (one every 2 MFMAs) in between.
+  // t+2 (one every 2 MFMAs over the first half, so that the last of them has
+  // the second half of QK and all of PV to land) and, when `with_softmax`,
+  // the softmax pieces of the previous tile (one every 2 MFMAs) in between.
   auto qk_tile = [&](int t, bool with_softmax) __attribute__((always_inline)) {
     const uint32_t cur = smem_base + (t % NBUF) * TILE_BYTES;
     uint32_t qb[4];  // per-tile base addresses; the chunk group goes in the immediate offset
@@ -642,7 +671,8 @@ void verify_attn_partial_kernel(PartialArgs a) {
       if (ks + QK_AHEAD < QK_STEPS) kbuf[ks % QK_AHEAD] = kread(ks + QK_AHEAD);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qf[ks], s, 0, 0, 0);
       if (ks == 2) gsrc = gather_src(slot_next);  // first needed at ks = 3
-      if ((ks & 3) == 3) load_to_lds16(gsrc + 64 * (ks >> 2), gdst + (ks >> 2) * GROUP_BYTES);
+      if ((ks & 1) == 1 && ks >= 3 && ks < 3 + 2 * CHUNK_GROUPS)  // ks = 3, 5, .., 19
+        load_to_lds16(gsrc + 64 * ((ks - 3) >> 1), gdst + ((ks - 3) >> 1) * GROUP_BYTES);
       if (with_softmax && (ks & 1) == 0 && (ks >> 1) < SM_PIECES) sm_piece(ks >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -679,10 +709,9 @@ void verify_attn_partial_kernel(PartialArgs a) {
     }
   };
 
-  // Tile 0: publish it (own loads of tile 0 and the slots of tile 2 landed;
-  // younger: the slots of tile 3, the gather of tile 1 and the late query
-  // fragments), then its QK (carrying the gather of tile 2).
-  wait_vmcnt<CHUNK_GROUPS + 1 + (QK_STEPS - Q_EARLY)>();
+  // Tile 0: publish it (every load of this wave so far has landed; the
+  // barrier also ends every wave's query reads from the staging region),
+  // then its QK (carrying the gather of tile 2).
   lds_barrier();  // tile 0 complete; ancestor masks visible
   sv = qk_tile(0, false);
   // Iteration it: QK of tile it+1 with the softmax of tile it in between, then

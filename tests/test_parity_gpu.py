@@ -100,6 +100,16 @@ def test_edge_shapes(orc, case):
     check_full(orc, small(**case))
 
 
+@pytest.mark.parametrize("B", [70, 130])
+def test_many_sequences(orc, B):
+    """More sequences than one 64-lane scan covers: the split location and the
+    combine's sequence lookup take their multi-pass path."""
+    rng = np.random.default_rng(B)
+    prefixes = [int(p) for p in rng.integers(0, 400, size=B)]
+    prefixes[B // 2] = 0
+    check_full(orc, small(B=B, H=2, T=4, prefixes=prefixes, seed=B))
+
+
 @pytest.mark.parametrize("tree", ["flat", "chain"])
 def test_tree_shapes(orc, tree):
     check_full(orc, small(H=4, T=64, prefixes=[300], tree=tree, seed=5))
