@@ -10,6 +10,9 @@ output rows); this module compiles it with gcc and calls it through ctypes.
 Parity status of each oracle function (pins live in tests/test_oracle_pins.py):
   oracle_verify_attn / oracle_verify_attn_rows: pinned (library attention with
       an explicit mask, closed forms, invariants, planted-mistake checks).
+  oracle_verify_attn_f32 / oracle_verify_attn_rows_f32 (binary32 q and KV):
+      pinned (library attention with an explicit mask on fp32 data; bit-equal
+      to the bf16 entry points when the fp32 values are bf16 values).
   oracle_row_weights: pinned (weights sum to 1, zero outside the visible set,
       match the library routine's attention probabilities).
   append_kv (NumPy, below): pinned (re-appending a workload's own tree rows
@@ -59,13 +62,19 @@ class Oracle:
         lib.oracle_row_weights.argtypes = [i32, i32, i32, vp, vp, i64, vp, vp, vp, dbl, i32, i32, i32,
                                            vp, vp]
         lib.oracle_row_weights.restype = i32
+        lib.oracle_verify_attn_f32.argtypes = lib.oracle_verify_attn.argtypes
+        lib.oracle_verify_attn_f32.restype = i32
+        lib.oracle_verify_attn_rows_f32.argtypes = lib.oracle_verify_attn_rows.argtypes
+        lib.oracle_verify_attn_rows_f32.restype = i32
         lib.oracle_num_threads.restype = i32
         self.lib = lib
 
     @staticmethod
     def _prep(q, kv_pool, slot_idx, seq_lens, tree_parent):
-        q = np.ascontiguousarray(q, dtype=np.uint16)
-        kv_pool = np.ascontiguousarray(kv_pool, dtype=np.uint16)
+        # bf16 bit patterns (uint16), or binary32 values for the fp32 entry points
+        dt = np.float32 if np.asarray(q).dtype == np.float32 else np.uint16
+        q = np.ascontiguousarray(q, dtype=dt)
+        kv_pool = np.ascontiguousarray(kv_pool, dtype=dt)
         slot_idx = np.ascontiguousarray(slot_idx, dtype=np.int32)
         seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
         tree_parent = np.ascontiguousarray(tree_parent, dtype=np.int32)
@@ -88,7 +97,8 @@ class Oracle:
         q, kv_pool, slot_idx, seq_lens, tree_parent, B, T, H = self._prep(
             q, kv_pool, slot_idx, seq_lens, tree_parent)
         out = np.empty((B, T, H, V_DIM), dtype=np.float64)
-        rc = self.lib.oracle_verify_attn(B, H, T, q.ctypes.data, kv_pool.ctypes.data,
+        fn = self.lib.oracle_verify_attn_f32 if q.dtype == np.float32 else self.lib.oracle_verify_attn
+        rc = fn(B, H, T, q.ctypes.data, kv_pool.ctypes.data,
                                          kv_pool.shape[0], slot_idx.ctypes.data,
                                          seq_lens.ctypes.data, tree_parent.ctypes.data,
                                          float(sm_scale), out.ctypes.data, int(nthreads))
@@ -102,7 +112,8 @@ class Oracle:
             q, kv_pool, slot_idx, seq_lens, tree_parent)
         rows = np.ascontiguousarray(rows_bth, dtype=np.int32).reshape(-1, 3)
         out = np.empty((rows.shape[0], V_DIM), dtype=np.float64)
-        rc = self.lib.oracle_verify_attn_rows(B, H, T, q.ctypes.data, kv_pool.ctypes.data,
+        fn = self.lib.oracle_verify_attn_rows_f32 if q.dtype == np.float32 else self.lib.oracle_verify_attn_rows
+        rc = fn(B, H, T, q.ctypes.data, kv_pool.ctypes.data,
                                               kv_pool.shape[0], slot_idx.ctypes.data,
                                               seq_lens.ctypes.data, tree_parent.ctypes.data,
                                               float(sm_scale), rows.shape[0], rows.ctypes.data,
@@ -115,6 +126,8 @@ class Oracle:
         """(weights over the sequence's seq_lens[b] keys, output row) for one (b, t, h)."""
         q, kv_pool, slot_idx, seq_lens, tree_parent, B, T, H = self._prep(
             q, kv_pool, slot_idx, seq_lens, tree_parent)
+        if q.dtype != np.uint16:
+            raise ValueError("row_weights takes bf16 inputs")
         w = np.empty(int(seq_lens[b]), dtype=np.float64)
         o = np.empty(V_DIM, dtype=np.float64)
         rc = self.lib.oracle_row_weights(B, H, T, q.ctypes.data, kv_pool.ctypes.data,

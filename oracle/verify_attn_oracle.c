@@ -28,7 +28,9 @@
  *
  * Layouts: q [B, T, H, 576] bf16 bits; kv_pool [pool_slots, 576] bf16 bits;
  * slot_idx int32 [sum seq_lens]; seq_lens int32 [B]; tree_parent int32 [B, T];
- * out fp64 [B, T, H, 512].
+ * out fp64 [B, T, H, 512]. The *_f32 entry points take q and kv_pool as IEEE
+ * binary32 values instead (the data type of the first, fp32 kernel of "The
+ * Checkpoint Report", Architecture of the Report); everything else is the same.
  *
  * The exponent is taken relative to the exact maximum (two passes), and the
  * sums run over j in increasing order.
@@ -58,6 +60,12 @@ static double bf16_to_double(uint16_t bits) {
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+}
+
+/* Element idx of a q or kv_pool array: bf16 bits, or binary32 when f32 != 0. */
+static double elem(const void* base, int64_t idx, int f32) {
+    if (f32) return (double)((const float*)base)[idx];
+    return bf16_to_double(((const uint16_t*)base)[idx]);
 }
 
 /* Check the host-side inputs the definition relies on. */
@@ -92,7 +100,7 @@ static void visible_set(int P, int T, int t, const int32_t* parent_b, unsigned c
  * seq_lens[b]. If weights != NULL it receives w_j for every j < seq_lens[b]
  * (0 for keys outside vis(t)).
  */
-static void attend_row(int B, int H, int T, const uint16_t* q, const uint16_t* kv_pool,
+static void attend_row(int B, int H, int T, const void* q, const void* kv_pool, int f32,
                        const int32_t* slot_idx, const int32_t* seq_lens, const int32_t* tree_parent,
                        double sm_scale, int b, int t, int h, double* scores, unsigned char* visible,
                        double* out_row, double* weights) {
@@ -103,17 +111,17 @@ static void attend_row(int B, int H, int T, const uint16_t* q, const uint16_t* k
     const int P = N - T;
     visible_set(P, T, t, tree_parent + (int64_t)b * T, visible);
 
-    const uint16_t* qrow = q + (((int64_t)b * T + t) * H + h) * KV_DIM;
+    const int64_t qrow = (((int64_t)b * T + t) * H + h) * KV_DIM;
     double qd[KV_DIM];
-    for (int d = 0; d < KV_DIM; ++d) qd[d] = bf16_to_double(qrow[d]);
+    for (int d = 0; d < KV_DIM; ++d) qd[d] = elem(q, qrow + d, f32);
 
     /* pass 1: scores and their maximum */
     double smax = -INFINITY;
     for (int j = 0; j < N; ++j) {
         if (!visible[j]) continue;
-        const uint16_t* krow = kv_pool + (int64_t)slot_idx[seg + j] * KV_DIM;
+        const int64_t krow = (int64_t)slot_idx[seg + j] * KV_DIM;
         double dot = 0.0;
-        for (int d = 0; d < KV_DIM; ++d) dot += qd[d] * bf16_to_double(krow[d]);
+        for (int d = 0; d < KV_DIM; ++d) dot += qd[d] * elem(kv_pool, krow + d, f32);
         scores[j] = sm_scale * dot;
         if (scores[j] > smax) smax = scores[j];
     }
@@ -127,8 +135,8 @@ static void attend_row(int B, int H, int T, const uint16_t* q, const uint16_t* k
         double w = visible[j] ? exp(scores[j] - smax) / denom : 0.0;
         if (weights) weights[j] = w;
         if (w == 0.0) continue;
-        const uint16_t* vrow = kv_pool + (int64_t)slot_idx[seg + j] * KV_DIM;
-        for (int d = 0; d < V_DIM; ++d) out_row[d] += w * bf16_to_double(vrow[d]);
+        const int64_t vrow = (int64_t)slot_idx[seg + j] * KV_DIM;
+        for (int d = 0; d < V_DIM; ++d) out_row[d] += w * elem(kv_pool, vrow + d, f32);
     }
 }
 
@@ -140,10 +148,10 @@ static int max_len(int B, const int32_t* seq_lens) {
 }
 
 /* Selected rows: rows_bth holds nrows triples (b, t, h); out is [nrows, 512]. */
-int oracle_verify_attn_rows(int B, int H, int T, const uint16_t* q, const uint16_t* kv_pool,
-                            int64_t pool_slots, const int32_t* slot_idx, const int32_t* seq_lens,
-                            const int32_t* tree_parent, double sm_scale, int64_t nrows,
-                            const int32_t* rows_bth, double* out, int nthreads) {
+static int verify_rows(int B, int H, int T, const void* q, const void* kv_pool, int f32,
+                       int64_t pool_slots, const int32_t* slot_idx, const int32_t* seq_lens,
+                       const int32_t* tree_parent, double sm_scale, int64_t nrows,
+                       const int32_t* rows_bth, double* out, int nthreads) {
     int rc = check_inputs(B, H, T, pool_slots, slot_idx, seq_lens, tree_parent);
     if (rc) return rc;
     for (int64_t r = 0; r < nrows; ++r) {
@@ -169,7 +177,7 @@ int oracle_verify_attn_rows(int B, int H, int T, const uint16_t* q, const uint16
 #pragma omp for schedule(dynamic, 1)
 #endif
             for (int64_t r = 0; r < nrows; ++r)
-                attend_row(B, H, T, q, kv_pool, slot_idx, seq_lens, tree_parent, sm_scale,
+                attend_row(B, H, T, q, kv_pool, f32, slot_idx, seq_lens, tree_parent, sm_scale,
                            rows_bth[3 * r], rows_bth[3 * r + 1], rows_bth[3 * r + 2], scores,
                            visible, out + r * V_DIM, NULL);
         }
@@ -179,10 +187,26 @@ int oracle_verify_attn_rows(int B, int H, int T, const uint16_t* q, const uint16
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 
+int oracle_verify_attn_rows(int B, int H, int T, const uint16_t* q, const uint16_t* kv_pool,
+                            int64_t pool_slots, const int32_t* slot_idx, const int32_t* seq_lens,
+                            const int32_t* tree_parent, double sm_scale, int64_t nrows,
+                            const int32_t* rows_bth, double* out, int nthreads) {
+    return verify_rows(B, H, T, q, kv_pool, 0, pool_slots, slot_idx, seq_lens, tree_parent,
+                       sm_scale, nrows, rows_bth, out, nthreads);
+}
+
+int oracle_verify_attn_rows_f32(int B, int H, int T, const float* q, const float* kv_pool,
+                                int64_t pool_slots, const int32_t* slot_idx, const int32_t* seq_lens,
+                                const int32_t* tree_parent, double sm_scale, int64_t nrows,
+                                const int32_t* rows_bth, double* out, int nthreads) {
+    return verify_rows(B, H, T, q, kv_pool, 1, pool_slots, slot_idx, seq_lens, tree_parent,
+                       sm_scale, nrows, rows_bth, out, nthreads);
+}
+
 /* Every row: out is [B, T, H, 512]. */
-int oracle_verify_attn(int B, int H, int T, const uint16_t* q, const uint16_t* kv_pool,
-                       int64_t pool_slots, const int32_t* slot_idx, const int32_t* seq_lens,
-                       const int32_t* tree_parent, double sm_scale, double* out, int nthreads) {
+static int verify_all(int B, int H, int T, const void* q, const void* kv_pool, int f32,
+                      int64_t pool_slots, const int32_t* slot_idx, const int32_t* seq_lens,
+                      const int32_t* tree_parent, double sm_scale, double* out, int nthreads) {
     const int64_t nrows = (int64_t)B * T * H;
     int32_t* rows = (int32_t*)malloc(sizeof(int32_t) * 3 * (size_t)nrows);
     if (!rows) return ORACLE_NO_MEMORY;
@@ -194,10 +218,24 @@ int oracle_verify_attn(int B, int H, int T, const uint16_t* q, const uint16_t* k
                 rows[3 * r + 1] = t;
                 rows[3 * r + 2] = h;
             }
-    int rc = oracle_verify_attn_rows(B, H, T, q, kv_pool, pool_slots, slot_idx, seq_lens,
-                                     tree_parent, sm_scale, nrows, rows, out, nthreads);
+    int rc = verify_rows(B, H, T, q, kv_pool, f32, pool_slots, slot_idx, seq_lens, tree_parent,
+                         sm_scale, nrows, rows, out, nthreads);
     free(rows);
     return rc;
+}
+
+int oracle_verify_attn(int B, int H, int T, const uint16_t* q, const uint16_t* kv_pool,
+                       int64_t pool_slots, const int32_t* slot_idx, const int32_t* seq_lens,
+                       const int32_t* tree_parent, double sm_scale, double* out, int nthreads) {
+    return verify_all(B, H, T, q, kv_pool, 0, pool_slots, slot_idx, seq_lens, tree_parent,
+                      sm_scale, out, nthreads);
+}
+
+int oracle_verify_attn_f32(int B, int H, int T, const float* q, const float* kv_pool,
+                           int64_t pool_slots, const int32_t* slot_idx, const int32_t* seq_lens,
+                           const int32_t* tree_parent, double sm_scale, double* out, int nthreads) {
+    return verify_all(B, H, T, q, kv_pool, 1, pool_slots, slot_idx, seq_lens, tree_parent,
+                      sm_scale, out, nthreads);
 }
 
 /* Softmax weights of one row: weights has seq_lens[b] entries; out_row 512. */
@@ -216,7 +254,7 @@ int oracle_row_weights(int B, int H, int T, const uint16_t* q, const uint16_t* k
         free(visible);
         return ORACLE_NO_MEMORY;
     }
-    attend_row(B, H, T, q, kv_pool, slot_idx, seq_lens, tree_parent, sm_scale, b, t, h, scores,
+    attend_row(B, H, T, q, kv_pool, 0, slot_idx, seq_lens, tree_parent, sm_scale, b, t, h, scores,
                visible, out_row, weights);
     free(scores);
     free(visible);

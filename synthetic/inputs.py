@@ -84,8 +84,8 @@ class Workload:
     T: int
     prefixes: list
     pool_slots: int
-    q: np.ndarray            # uint16 [B, T, H, 576] (bf16 bits)
-    kv_pool: np.ndarray      # uint16 [pool_slots, 576]
+    q: np.ndarray            # uint16 [B, T, H, 576] (bf16 bits), or float32 values
+    kv_pool: np.ndarray      # uint16 [pool_slots, 576] (bf16 bits), or float32 values
     slot_idx: np.ndarray     # int32 [sum_b (P_b + T)]
     seq_lens: np.ndarray     # int32 [B] = P_b + T
     tree_parent: np.ndarray  # int32 [B, T]
@@ -105,9 +105,14 @@ class Workload:
     def max_seq_len(self) -> int:
         return int(self.seq_lens.max())
 
+    @property
+    def f32(self) -> bool:
+        """True for fp32 q / kv_pool (values), False for bf16 (bit patterns)."""
+        return self.q.dtype == np.float32
+
     def kv_bytes(self) -> int:
         """Bytes of KV rows one call touches (each referenced row once)."""
-        return self.total_kv * KV_DIM * 2
+        return self.total_kv * KV_DIM * self.kv_pool.itemsize
 
 
 def make_workload(
@@ -125,6 +130,7 @@ def make_workload(
     kv_std: float = 0.1,
     sm_scale: float = DEFAULT_SCALE,
     layout: str = "scattered",
+    dtype: str = "bf16",
 ) -> Workload:
     """Build one seeded workload.
 
@@ -133,6 +139,8 @@ def make_workload(
     slots, sequences take consecutive slices of it: prefix rows then tree rows),
     or "contiguous" (the same row values moved so that the slot list of all
     sequences is 0, 1, 2, ...; page_size=64).
+    ``dtype``: "bf16" (values rounded to nearest even, stored as bit patterns)
+    or "f32" (the same draws kept as binary32 values).
     """
     prefixes = [int(p) for p in prefixes]
     assert len(prefixes) == B and T >= 1
@@ -142,9 +150,11 @@ def make_workload(
     ss = np.random.SeedSequence(seed)
     s_pool, s_perm, s_tree, s_q = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(4)]
 
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(dtype)
     pool32 = s_pool.standard_normal((pool_slots, KV_DIM), dtype=np.float32)
     pool32 *= np.float32(kv_std)
-    kv_pool = f32_to_bf16_bits(pool32)
+    kv_pool = pool32 if dtype == "f32" else f32_to_bf16_bits(pool32)
     del pool32
 
     perm = s_perm.permutation(pool_slots).astype(np.int64)
@@ -165,7 +175,7 @@ def make_workload(
     q32 = s_q.standard_normal((B, T, H, KV_DIM), dtype=np.float32)
     if q_std != 1.0:
         q32 *= np.float32(q_std)
-    q = f32_to_bf16_bits(q32)
+    q = q32 if dtype == "f32" else f32_to_bf16_bits(q32)
 
     page_size = 1
     if layout == "contiguous":
@@ -200,6 +210,9 @@ CONFIGS = {
                       seed=5000),
     "e1_h64_65k": dict(B=1, H=64, T=64, prefixes=[65536], pool_slots=131072, seed=6000),
     "e2_h8_t9_65k": dict(B=1, H=8, T=9, prefixes=[65536], pool_slots=131072, seed=7000),
+    # fp32 inputs (binary32 q and KV pool) at the 64k-token H=8 shape
+    "f4_long_f32": dict(B=1, H=8, T=64, prefixes=[65536], pool_slots=131072, seed=4000,
+                        dtype="f32"),
 }
 
 

@@ -22,8 +22,11 @@ from synthetic import inputs
 KV, DV = 576, 512
 
 
-def _f64(bits):
-    return inputs.bf16_bits_to_f32(bits).astype(np.float64)
+def _f64(x):
+    """fp64 values of bf16 bit patterns (uint16) or of binary32 values."""
+    if x.dtype == np.float32:
+        return x.astype(np.float64)
+    return inputs.bf16_bits_to_f32(x).astype(np.float64)
 
 
 def ancestor_closure(parent: np.ndarray) -> np.ndarray:
@@ -326,9 +329,36 @@ def pin_worked_example(orc):
         assert not np.any(out[0, t, 0, 2:]), t
 
 
+def pin_f32_library_attention(orc):
+    """fp32 inputs (the binary32 entry points): oracle == library attention with
+    an explicit mask, on the same draws kept unrounded."""
+    cases = [
+        dict(B=1, H=1, T=1, prefixes=[0]), dict(B=1, H=2, T=3, prefixes=[5]),
+        dict(B=2, H=2, T=8, prefixes=[0, 64]), dict(B=1, H=2, T=64, prefixes=[64]),
+        dict(B=3, H=1, T=3, prefixes=[1, 5, 17]),
+    ]
+    for i, c in enumerate(cases):
+        wl = tiny(seed=300 + i, dtype="f32", **c)
+        assert wl.q.dtype == np.float32
+        got = run(orc, wl)
+        ref = library_attention(wl)
+        err = np.abs(got - ref).max()
+        assert err <= 1e-13, f"f32 case {c}: max |oracle - library| = {err}"
+
+
+def pin_f32_on_bf16_values(orc):
+    """binary32 arrays that hold bf16 values give exactly the bf16 result."""
+    import dataclasses
+    wl = tiny(B=2, H=2, T=8, prefixes=[17, 3], seed=7)
+    wl32 = dataclasses.replace(wl, q=inputs.bf16_bits_to_f32(wl.q),
+                               kv_pool=inputs.bf16_bits_to_f32(wl.kv_pool))
+    assert wl32.q.dtype == np.float32
+    assert np.array_equal(run(orc, wl), run(orc, wl32))
+
+
 ALL_PINS = [
     pin_library_attention, pin_flat_tree_is_decode, pin_chain_tree_is_causal,
     pin_zero_query_is_mean, pin_single_key, pin_weights, pin_slot_permutation,
     pin_tree_relabel, pin_head_subset, pin_sequences_independent, pin_constant_column,
-    pin_scale_linear, pin_worked_example,
+    pin_scale_linear, pin_worked_example, pin_f32_library_attention, pin_f32_on_bf16_values,
 ]

@@ -28,8 +28,12 @@ MUTATIONS = {
     "q_head_node_transposed": ("(((int64_t)b * T + t) * H + h) * KV_DIM",
                                "(((int64_t)b * H + h) * T + t) * KV_DIM"),
     "scale_applied_twice": ("scores[j] = sm_scale * dot;", "scores[j] = sm_scale * sm_scale * dot;"),
-    "value_from_wrong_columns": ("out_row[d] += w * bf16_to_double(vrow[d]);",
-                                 "out_row[d] += w * bf16_to_double(vrow[d + 64]);"),
+    "value_from_wrong_columns": ("out_row[d] += w * elem(kv_pool, vrow + d, f32);",
+                                 "out_row[d] += w * elem(kv_pool, vrow + d + 64, f32);"),
+    "f32_elements_swapped": ("if (f32) return (double)((const float*)base)[idx];",
+                             "if (f32) return (double)((const float*)base)[idx ^ 1];"),
+    "f32_read_as_bf16": ("if (f32) return (double)((const float*)base)[idx];",
+                         "if (f32) return bf16_to_double(((const uint16_t*)base)[idx]);"),
     "bf16_widening_wrong": ("uint32_t u = ((uint32_t)bits) << 16;",
                             "uint32_t u = ((uint32_t)bits) << 15;"),
     "denominator_misses_tree": ("if (visible[j]) denom += exp(scores[j] - smax);",
