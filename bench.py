@@ -37,6 +37,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 MALL_BYTES = 256 << 20
 KV_ROW_BYTES = 576 * 2
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
 FLOPS_PER_KEY_ROW = 2 * 576 + 2 * 512  # QK^T + PV per (KV row, query row)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_partial_c4a.json")
 KERNEL_SRC = os.path.join(ROOT, "mla_tree_verify_latent_amd", "csrc", "verify_attn.hip")
@@ -51,6 +52,8 @@ WORKLOAD_TEXT = {
     "e2_h8_t9_65k": "production shape: H=8, 1 sequence, prefix 65536, T=9, scattered",
     "c2_tp_share": "TP-share decode verify: H=8, prefix 4096, T=32, 65536-slot pool",
     "c3_full_head": "full-head verify: H=64, prefix 16384, T=32, 131072-slot pool",
+    "f4_long_f32": "fp32 inputs: H=8, 1 sequence, prefix 65536, T=64, scattered, binary32 q and "
+                   "[131072, 576] KV pool, fp32 output",
 }
 
 
@@ -58,7 +61,8 @@ def algorithmic_bytes(wl) -> int:
     """Bytes one call must move at least: each referenced KV row and its slot index once,
     q and out once, the tree and the sequence lengths once."""
     rows = wl.total_kv
-    return (rows * (KV_ROW_BYTES + 4) + wl.B * wl.T * wl.H * (576 + 512) * 2
+    elt = wl.kv_pool.itemsize  # 2 (bf16) or 4 (fp32)
+    return (rows * (576 * elt + 4) + wl.B * wl.T * wl.H * (576 + 512) * elt
             + wl.B * wl.T * 4 + wl.B * 4)
 
 
@@ -81,8 +85,8 @@ class Bench:
         self.torch, self.mtv, self.wl = torch, mtv, wl
         base = to_device(wl)
         self.params = params_of(wl, nsplit)
-        self.ws = torch.empty(mtv.verify_attn_workspace_size(self.params), dtype=torch.uint8,
-                              device="cuda")
+        wsize = (mtv.verify_attn_f32_workspace_size if wl.f32 else mtv.verify_attn_workspace_size)(self.params)
+        self.ws = torch.empty(wsize, dtype=torch.uint8, device="cuda")
         self.reps = []
         for r in range(replicas):
             d = dict(base)
@@ -90,14 +94,19 @@ class Bench:
                 d["kv_pool"] = base["kv_pool"].clone()
                 d["q"] = base["q"].clone()
             self.reps.append(d)
-        self.out = torch.empty((wl.B, wl.T, wl.H, 512), dtype=torch.bfloat16, device="cuda")
+        self.out = torch.empty((wl.B, wl.T, wl.H, 512), dtype=torch.float32 if wl.f32 else torch.bfloat16,
+                               device="cuda")
         self.kv_new = torch.zeros((wl.B, wl.T, 576), dtype=torch.bfloat16, device="cuda")
         self.kv_dst = None
         torch.cuda.synchronize()
 
     def call(self, r, stage="full"):
         d = self.reps[r % len(self.reps)]
-        if stage == "full":
+        if self.wl.f32:  # the fp32-input path has one entry point (partial + combine)
+            assert stage == "full", stage
+            self.mtv.verify_attn_f32(d["q"], d["kv_pool"], d["slot_idx"], d["seq_lens"],
+                                     d["tree_parent"], self.out, self.ws, self.params)
+        elif stage == "full":
             self.mtv.verify_attn(d["q"], d["kv_pool"], d["slot_idx"], d["seq_lens"],
                                  d["tree_parent"], self.out, self.ws, self.params)
         elif stage == "partial":
@@ -158,7 +167,8 @@ def measure(name, steps, warmup, nsplit=0, stages=("full", "partial")):
     wl = inputs.config(name)
     R = replicas_for(wl)
     b = Bench(wl, R, nsplit)
-    res = {"workload": name, "replicas": R, "plan": b.mtv.verify_attn_plan(b.params)}
+    res = {"workload": name, "replicas": R,
+           "plan": None if wl.f32 else b.mtv.verify_attn_plan(b.params)}
     for st in stages:
         ms, all_ms = b.time_graph(steps, warmup, st)
         res[f"{st}_ms"] = ms
@@ -258,6 +268,7 @@ def main():
     ap.add_argument("--extras", default="c4b_long_contiguous,e2_h8_t9_65k,e1_h64_65k,c5_ragged",
                     help="comma-separated extra workloads reported beside the headline ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-f32", action="store_true", help="skip the fp32-input variant line")
     ap.add_argument("--stage", default=None, choices=[None, "full", "partial", "combine", "append", "compact", "copy"],
                     help="profiling aid: only run K calls of one stage of the headline workload; "
                          "'copy' runs K device-to-device copies of 1 GiB (counter calibration)")
@@ -314,7 +325,7 @@ def main():
     part_tflops = head["flops"] / (part_ms * 1e-3) / 1e12
     extras = {}
     for name in [e for e in args.extras.split(",") if e]:
-        r = measure(name, max(10, args.steps // 4), max(2, args.warmup // 4))
+        r = measure(name, args.steps, args.warmup)
         extras[name] = {
             "workload": WORKLOAD_TEXT.get(name, name),
             "ms_per_call": round(r["full_ms"], 5),
@@ -325,6 +336,20 @@ def main():
             "partial_mfma_tflops": round(r["flops"] / (r["partial_ms"] * 1e-3) / 1e12, 1),
             "mfma_frac": round(r["flops"] / (r["partial_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "ms_per_call_mall_warm": round(r["full_ms_mall_warm"], 5),
+            "replicas": r["replicas"],
+        }
+        torch.cuda.empty_cache()
+
+    f32 = None
+    if not args.no_f32:
+        r = measure("f4_long_f32", args.steps, args.warmup, stages=("full",))
+        f32 = {
+            "workload": WORKLOAD_TEXT["f4_long_f32"],
+            "ms_per_call": round(r["full_ms"], 5),
+            "calls_per_s": round(1e3 / r["full_ms"], 1),
+            "hbm_gbs": round(r["bytes"] / (r["full_ms"] * 1e-3) / 1e9, 1),
+            "mfma_f32_tflops": round(r["flops"] / (r["full_ms"] * 1e-3) / 1e12, 1),
+            "mfma_f32_frac": round(r["flops"] / (r["full_ms"] * 1e-3) / 1e12 / MFMA_F32_PEAK_TFLOPS, 4),
             "replicas": r["replicas"],
         }
         torch.cuda.empty_cache()
@@ -369,6 +394,8 @@ def main():
             "us_per_call": round(head["append_ms"] * 1e3, 2),
             "gbs": round(2 * KV_ROW_BYTES * head["wl"].B * head["wl"].T / (head["append_ms"] * 1e-3) / 1e9, 1),
         },
+        # fp32-input variant (whole call, partial + combine) on the same shape in binary32
+        "f32_variant": f32,
         # KV defragmentation on the same workload: total_kv rows of 1,152 B gathered and written
         "compact_kv": {
             "rows": head["wl"].total_kv,

@@ -168,6 +168,25 @@ int verify_attn_append_kv(const verify_attn_params* p, const void* kv_new, const
                           const int32_t* seq_lens, void* kv_pool, void* stream);
 
 /*
+ * fp32-input variant ("The Checkpoint Report", Architecture of the Report: the
+ * first kernel of the pages took fp32 data with 16-byte vector loads): the same
+ * operation as verify_attn on binary32 q and KV rows, computed in fp32
+ * throughout (MFMA 16x16x4 f32; the softmax weights stay fp32), fp32 output.
+ *   q        float [B, T, H, 576], 16-byte aligned
+ *   kv_pool  float [pool_slots, 576] (2,304-byte rows), 16-byte aligned
+ *   out      float [B, T, H, 512], 16-byte aligned
+ *   slot_idx, seq_lens, tree_parent, p: as for verify_attn.
+ *   workspace: at least verify_attn_f32_workspace_size(p) bytes, 16-byte
+ *   aligned (caller-owned; its own size, not verify_attn_workspace_size).
+ * Two kernels on `stream`; no allocation, no host synchronisation (graph
+ * capturable). Status codes as for verify_attn.
+ */
+size_t verify_attn_f32_workspace_size(const verify_attn_params* p);
+int verify_attn_f32(const verify_attn_params* p, const float* q, const float* kv_pool, const int32_t* slot_idx,
+                    const int32_t* seq_lens, const int32_t* tree_parent, float* out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
  * KV defragmentation: copy every referenced latent row into consecutive rows,
  *   kv_dst[i] = kv_pool[slot_idx[i]]   for i < total_kv,
  * i.e. each sequence's KV (prefix rows, then its tree nodes' rows) becomes one
@@ -187,10 +206,11 @@ int verify_attn_compact_kv(const verify_attn_params* p, const void* kv_pool, con
 /* Static description of a status code (never NULL). */
 const char* verify_attn_strerror(int status);
 
-/* ABI version of this header: (major << 16) | minor (minor 1: verify_attn_append_kv; 2: verify_attn_compact_kv). */
+/* ABI version of this header: (major << 16) | minor (minor 1: verify_attn_append_kv; 2: verify_attn_compact_kv;
+   3: verify_attn_f32). */
 int verify_attn_version(void);
 
-#define VERIFY_ATTN_VERSION ((1 << 16) | 2)
+#define VERIFY_ATTN_VERSION ((1 << 16) | 3)
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,8 @@ raise.
 
 Entry points mirror the C ABI declared in ``include/verify_attn.h``:
 ``verify_attn``, ``verify_attn_partial``, ``verify_attn_combine``,
-``verify_attn_append_kv``, ``verify_attn_compact_kv``, ``verify_attn_workspace_size``, ``verify_attn_plan``,
+``verify_attn_append_kv``, ``verify_attn_compact_kv``, ``verify_attn_f32``,
+``verify_attn_f32_workspace_size``, ``verify_attn_workspace_size``, ``verify_attn_plan``,
 ``verify_attn_strerror``, ``verify_attn_version``.
 """
 from __future__ import annotations
@@ -26,7 +27,7 @@ MAX_TREE = 64
 
 EXPORTS = (
     "verify_attn", "verify_attn_partial", "verify_attn_combine", "verify_attn_append_kv",
-    "verify_attn_compact_kv",
+    "verify_attn_compact_kv", "verify_attn_f32", "verify_attn_f32_workspace_size",
     "verify_attn_workspace_size",
     "verify_attn_plan", "verify_attn_strerror", "verify_attn_version",
 )
@@ -76,6 +77,10 @@ def load_library(path: str = LIB_PATH):
     lib.verify_attn_workspace_size.restype = ctypes.c_size_t
     lib.verify_attn.argtypes = [P, vp, vp, i32p, i32p, i32p, vp, vp, ctypes.c_size_t, vp]
     lib.verify_attn.restype = ctypes.c_int
+    lib.verify_attn_f32.argtypes = [P, vp, vp, i32p, i32p, i32p, vp, vp, ctypes.c_size_t, vp]
+    lib.verify_attn_f32.restype = ctypes.c_int
+    lib.verify_attn_f32_workspace_size.argtypes = [P]
+    lib.verify_attn_f32_workspace_size.restype = ctypes.c_size_t
     lib.verify_attn_partial.argtypes = [P, vp, vp, i32p, i32p, i32p, vp, ctypes.c_size_t, vp]
     lib.verify_attn_partial.restype = ctypes.c_int
     lib.verify_attn_combine.argtypes = [P, i32p, vp, vp, ctypes.c_size_t, vp]
@@ -136,8 +141,9 @@ def _stream(stream) -> int:
     return int(stream.cuda_stream)
 
 
-def _check_tensors(q, kv_pool, slot_idx, seq_lens, tree_parent, out=None):
+def _check_tensors(q, kv_pool, slot_idx, seq_lens, tree_parent, out=None, dtype=None):
     import torch
+    dtype = torch.bfloat16 if dtype is None else dtype
     named = dict(q=q, kv_pool=kv_pool, slot_idx=slot_idx, seq_lens=seq_lens,
                  tree_parent=tree_parent)
     if out is not None:
@@ -148,8 +154,8 @@ def _check_tensors(q, kv_pool, slot_idx, seq_lens, tree_parent, out=None):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     for name in ("q", "kv_pool") + (("out",) if out is not None else ()):
-        if named[name].dtype != torch.bfloat16:
-            raise ValueError(f"{name} must be bfloat16")
+        if named[name].dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}")
     for name in ("slot_idx", "seq_lens", "tree_parent"):
         if named[name].dtype != torch.int32:
             raise ValueError(f"{name} must be int32")
@@ -178,6 +184,21 @@ def verify_attn(q, kv_pool, slot_idx, seq_lens, tree_parent, out, workspace, par
     """Enqueue the verify attention on `stream` (default: torch's current stream)."""
     _check_tensors(q, kv_pool, slot_idx, seq_lens, tree_parent, out)
     _check(load_library().verify_attn(
+        ctypes.byref(params), _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
+        _ptr(tree_parent), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def verify_attn_f32_workspace_size(params: Params) -> int:
+    return int(load_library().verify_attn_f32_workspace_size(ctypes.byref(params)))
+
+
+def verify_attn_f32(q, kv_pool, slot_idx, seq_lens, tree_parent, out, workspace, params: Params,
+                    stream=None) -> None:
+    """Enqueue the fp32-input verify attention (float32 q, kv_pool and out)."""
+    import torch
+    _check_tensors(q, kv_pool, slot_idx, seq_lens, tree_parent, out, dtype=torch.float32)
+    _check(load_library().verify_attn_f32(
         ctypes.byref(params), _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
         _ptr(tree_parent), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))

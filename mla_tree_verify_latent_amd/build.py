@@ -25,9 +25,9 @@ FLAGS = [
 
 
 def check_registers(extra=()) -> dict:
-    """Compile the device code to assembly and check the partial kernel's
-    register allocation: no spills, and exactly the 256 AGPRs of the output
-    accumulators (the asm MFMAs rely on the compiler never touching them)."""
+    """Compile the device code to assembly and check the partial kernels'
+    register allocation: no spills, and the AGPRs of the output accumulators
+    (the asm MFMAs rely on the compiler never touching them)."""
     with tempfile.TemporaryDirectory() as tmp:
         asm = os.path.join(tmp, "verify_attn.s")
         cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC", "-Werror")], *extra,
@@ -46,12 +46,17 @@ def check_registers(extra=()) -> dict:
             "vgpr_spill": int(re.search(r"\.vgpr_spill_count:\s+(\d+)", block).group(1)),
             "sgpr_spill": int(re.search(r"\.sgpr_spill_count:\s+(\d+)", block).group(1)),
         }
-    partial = [v for k, v in info.items() if "partial" in k]
-    if len(partial) != 1:
-        raise RuntimeError(f"partial kernel not found in the assembly metadata: {sorted(info)}")
-    p = partial[0]
-    if p["vgpr_spill"] or p["sgpr_spill"] or p["agpr"] != 256:
-        raise RuntimeError(f"partial kernel register allocation changed: {p}")
+    # bf16 kernel: 256 output accumulators; fp32 kernel: 128 (the compiler may
+    # round the AGPR block up). Neither may spill.
+    need = {"verify_attn_partial_kernel": lambda n: n == 256,
+            "verify_attn_f32_partial_kernel": lambda n: n >= 128}
+    for kname, agpr_ok in need.items():
+        found = [v for k, v in info.items() if kname + "E" in k]
+        if len(found) != 1:
+            raise RuntimeError(f"{kname} not found in the assembly metadata: {sorted(info)}")
+        p = found[0]
+        if p["vgpr_spill"] or p["sgpr_spill"] or not agpr_ok(p["agpr"]):
+            raise RuntimeError(f"{kname} register allocation changed: {p}")
     return info
 
 

@@ -117,7 +117,8 @@ struct CombineArgs {
   const float* part_o;
   const float* part_ml;
   const int32_t* seq_lens;
-  uint16_t* out;
+  uint16_t* out;      // bf16 output, or
+  float* out_f32;     // fp32 output (fp32-input path)
   int B, T, M, chunk, max_splits, max_seq_len;
 };
 
@@ -763,6 +764,299 @@ void verify_attn_partial_kernel(PartialArgs a) {
   }
 }
 
+// ------------------------------------------------- fp32-input partial kernel
+//
+// The same split-K partial results as verify_attn_partial_kernel, for binary32
+// q and KV rows (the data type of the first, fp32 kernel of "The Checkpoint
+// Report", Architecture of the Report), computed in fp32 throughout on MFMA
+// 16x16x4 f32: no operand is rounded to a narrower type, the softmax weights
+// included. The output partials have the same layout, so the same combine
+// merges them (with an fp32 output).
+//
+// One workgroup = 4 waves x 16 query rows (64 rows of one sequence) x one
+// split; one workgroup per CU. LDS: a ring of 3 KV tiles of 16 rows (36 KB
+// each: 2,304 bytes per row). Row r of a tile, 16-byte piece c (0..143) lives
+// at r * 2304 + (c ^ (r % 16)) * 16 (the XOR stays inside aligned groups of
+// 16 pieces). Wave w gathers rows 4w .. 4w+3 of each tile with nine
+// direct-to-LDS loads of 1 KB (consecutive LDS bytes, so lane -> (row, piece)
+// follows the layout).
+//
+// Per wave, per tile (16 query rows n, 16 keys m), MFMA 16x16x4 f32 with the
+// reduction index k = lane group g = lane / 16:
+//   S^T[m, n] += K[m, f] Q[n, f]    f = 16 c + 4 g + i, MFMA step (c, i):
+//     lane (m = l%16, g) gives K[m, f] (one 16-byte LDS read per chunk c
+//     serves 4 steps) and Q[n = l%16, f] (held in 144 VGPRs); lane l then
+//     holds S for row l%16, keys 4 g + i.
+//   O^T[e, n] += V[k, e] P[n, k]    k = 4 g + i, step i, 16-feature block e0:
+//     B = P is the lane's own weight for key 4 g + i (no exchange), A = V
+//     from one 4-byte LDS read per lane. O (128 fp32 per lane: row l%16,
+//     features 16 e0 + 4 g + i) stays in AGPRs.
+// The XOR layout keeps both read patterns free of bank conflicts: the 16-byte
+// K reads of 8 consecutive rows land on 8 distinct positions of a 128-byte
+// window, and the 4-byte V reads of keys 4g + i (g = 0..3) on distinct banks.
+constexpr int F_NK = 16;                          // keys per tile
+constexpr int F_ROWS_PER_WAVE = 16;               // query rows per wave (MFMA N)
+constexpr int F_ROWS_PER_TILE = NWAVES * F_ROWS_PER_WAVE;  // 64
+constexpr int F_ROW_BYTES = KV_DIM * 4;           // 2,304
+constexpr int F_TILE_BYTES = F_NK * F_ROW_BYTES;  // 36 KB
+constexpr int F_NBUF = 3;
+constexpr int F_PIECES = KV_DIM / 4;              // 144 16-byte pieces per row
+constexpr int F_CHUNKS = KV_DIM / 16;             // 36 QK chunks of 16 features
+constexpr int F_LOADS = F_NK / NWAVES * F_ROW_BYTES / 1024;  // 9 gather loads per wave and tile
+constexpr int F_PV_BLOCKS = V_DIM / 16;           // 32 blocks of 16 features
+static_assert(F_PIECES % 16 == 0, "the piece XOR stays inside a row");
+static_assert(F_LOADS * 1024 == F_NK / NWAVES * F_ROW_BYTES, "whole loads per band");
+
+struct PartialF32Args {
+  const float* q;
+  const float* kv;
+  const int32_t* slot_idx;
+  const int32_t* seq_lens;
+  const int32_t* tree_parent;
+  float* part_o;
+  float* part_ml;
+  int B, H, T, M;
+  int row_tiles, chunk, max_splits, max_seq_len;
+  int64_t total_kv, pool_slots;
+  float qk_scale_log2;
+};
+
+__device__ __forceinline__ void mfma16_acc(f32x4& acc, float a, float b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x4_f32 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void acc_scale4(f32x4& acc, float s) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(acc[i]), "=&v"(tmp)
+                 : "v"(s));
+  }
+}
+
+__global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void verify_attn_f32_partial_kernel(PartialF32Args a) {
+  __shared__ __attribute__((aligned(1024))) char smem[F_NBUF * F_TILE_BYTES];
+  __shared__ unsigned long long anc_s[MAX_TREE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int g, rt;
+  SplitLoc loc;
+  if (!locate_item(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, a.max_splits, a.row_tiles, &g, &rt, &loc)) return;
+  g = __builtin_amdgcn_readfirstlane(g);
+  rt = __builtin_amdgcn_readfirstlane(rt);
+  loc.b = __builtin_amdgcn_readfirstlane(loc.b);
+  loc.len = __builtin_amdgcn_readfirstlane(loc.len);
+  loc.seg = ((int64_t)__builtin_amdgcn_readfirstlane((int)(loc.seg >> 32)) << 32) |
+            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)loc.seg);
+  const int k0 = (g - __builtin_amdgcn_readfirstlane(loc.g0)) * a.chunk;
+  const int k1 = min(k0 + a.chunk, loc.len);
+  const int P = loc.len - a.T;
+  const int ntiles = (k1 - k0 + F_NK - 1) / F_NK;
+  const uint32_t smem_base = lds_addr(smem);
+  const int64_t slot_hi = a.total_kv - 1;
+  const int pool_hi = (int)(a.pool_slots - 1 < (int64_t)INT32_MAX ? a.pool_slots - 1 : (int64_t)INT32_MAX);
+  const int grp = lane >> 4;  // reduction lane group
+  const int l16 = lane & 15;
+
+  // Gather of one tile: load j, lane -> LDS byte 1024 j + 16 lane of this
+  // wave's 4-row band -> (row, position) -> piece position ^ (row % 16).
+  int g_row[F_LOADS], g_piece[F_LOADS];
+#pragma unroll
+  for (int j = 0; j < F_LOADS; ++j) {
+    const int o = j * 1024 + 16 * lane;
+    const int lr = o / F_ROW_BYTES;
+    const int r = wave * (F_NK / NWAVES) + lr;
+    g_row[j] = lr;
+    g_piece[j] = ((o - lr * F_ROW_BYTES) >> 4) ^ (r & 15);
+  }
+  // Slot of row lr (0..3) of this wave's band of the tile at key kt; keys past
+  // the split end repeat its last key.
+  auto band_slot = [&](int kt, int lr) {
+    int key = kt + wave * (F_NK / NWAVES) + lr;
+    key = key < k1 ? key : k1 - 1;
+    int64_t si = loc.seg + key;
+    si = si < slot_hi ? si : slot_hi;
+    int slot = a.slot_idx[si];
+    return slot < 0 ? 0 : (slot > pool_hi ? pool_hi : slot);
+  };
+  auto gather = [&](int t, const int (&slots)[4]) {
+    const uint32_t dst = smem_base + (t % F_NBUF) * F_TILE_BYTES + wave * (F_NK / NWAVES) * F_ROW_BYTES;
+#pragma unroll
+    for (int j = 0; j < F_LOADS; ++j) {
+      const int lr = g_row[j];
+      const int slot = lr == 0 ? slots[0] : (lr == 1 ? slots[1] : (lr == 2 ? slots[2] : slots[3]));
+      load_to_lds16(a.kv + (int64_t)slot * KV_DIM + 4 * g_piece[j], dst + j * 1024);
+    }
+  };
+
+  // Prologue: parent pointers, the slots and gathers of tiles 0 and 1, the
+  // query fragments, the ancestor masks.
+  int parent = -1;
+  if (wave == 0 && lane < a.T) parent = a.tree_parent[(int64_t)loc.b * a.T + lane];
+  {
+    int s0[4], s1[4];
+#pragma unroll
+    for (int lr = 0; lr < 4; ++lr) {
+      s0[lr] = band_slot(k0, lr);
+      s1[lr] = band_slot(k0 + F_NK, lr);
+    }
+    gather(0, s0);
+    gather(1, s1);
+  }
+  const int row0 = rt * F_ROWS_PER_TILE + wave * F_ROWS_PER_WAVE;
+  const bool wave_active = row0 < a.M;
+  const int qrow = row0 + l16;
+  const bool row_ok = qrow < a.M;
+  f32x4 qf[F_CHUNKS];
+  {
+    const float* src = a.q + ((int64_t)loc.b * a.M + (row_ok ? qrow : 0)) * KV_DIM + 4 * grp;
+#pragma unroll
+    for (int c = 0; c < F_CHUNKS; ++c) {
+      f32x4 v = *reinterpret_cast<const f32x4*>(src + 16 * c);
+      qf[c] = row_ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  if (wave == 0) {  // ancestor masks by pointer jumping (as in the bf16 kernel)
+    int up = (parent >= 0 && parent < lane && lane < a.T) ? parent : -1;
+    unsigned long long m = lane < a.T ? (1ull << lane) : 0ull;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const int src = up >= 0 ? up : lane;
+      const unsigned long long m_up = __shfl(m, src);
+      const int up_up = __shfl(up, src);
+      if (up >= 0) {
+        m |= m_up;
+        up = up_up;
+      }
+    }
+    if (lane < a.T) anc_s[lane] = m;
+  }
+
+  // K read (chunk c): lane (key l16, group grp) reads piece 4c + grp of key
+  // row l16, stored at position (4c + grp) ^ l16 = 16 (c / 4) + 4 ((c % 4) ^ (l16 / 4))
+  // + (grp ^ (l16 % 4)): a per-lane base for each c % 4 plus 256 (c / 4).
+  uint32_t k_off[4];
+#pragma unroll
+  for (int c3 = 0; c3 < 4; ++c3)
+    k_off[c3] = l16 * F_ROW_BYTES + ((((c3 ^ (l16 >> 2)) << 2) | (grp ^ (l16 & 3))) << 4);
+  // V read (key step i, feature block e): lane (feature 16 e + l16, group grp)
+  // reads float l16 % 4 of piece 4 e + l16 / 4 of key row r = 4 grp + i, at
+  // position (4 e + l16 / 4) ^ r = 16 (e / 4) + 4 ((e % 4) ^ grp) + ((l16 / 4) ^ i):
+  // a per-lane base for each (i, e % 4) plus 256 (e / 4).
+  uint32_t v_off[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e3 = 0; e3 < 4; ++e3)
+      v_off[i][e3] = (4 * grp + i) * F_ROW_BYTES + ((((e3 ^ grp) << 2) | ((l16 >> 2) ^ i)) << 4) + 4 * (l16 & 3);
+  // V read (block e0, step i): lane (feature 16 e0 + l16, group grp) reads
+  // float l16 % 4 of piece 4 e0 + l16 / 4 of key row 4 grp + i.
+  f32x4 o[F_PV_BLOCKS];
+#pragma unroll
+  for (int e = 0; e < F_PV_BLOCKS; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int it = 0; it < ntiles; ++it) {
+    wait_vmcnt<0>();  // own share of tile it (and of it+1) landed
+    lds_barrier();    // tile it complete; every wave is done with tile it-1
+    const uint32_t cur = smem_base + (it % F_NBUF) * F_TILE_BYTES;
+    const int kt = k0 + it * F_NK;
+    // slots of tile it+2 (their gather goes out halfway through this QK)
+    int sn[4];
+    const bool more = it + 2 < ntiles;
+#pragma unroll
+    for (int lr = 0; lr < 4; ++lr) sn[lr] = band_slot(more ? kt + 2 * F_NK : kt, lr);
+    // ---- S^T = K Q^T: 36 chunks x 4 MFMAs, two accumulators (even / odd chunks)
+    f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    uint32_t kb[4];  // per-tile bases; chunk c reads kb[c % 4] + 256 (c / 4)
+#pragma unroll
+    for (int c3 = 0; c3 < 4; ++c3) kb[c3] = cur + k_off[c3];
+    auto kread = [&](int c) { return *(const LDS_AS f32x4*)(uintptr_t)(kb[c & 3] + 256 * (c >> 2)); };
+    f32x4 kbuf[QK_AHEAD];
+#pragma unroll
+    for (int c = 0; c < QK_AHEAD; ++c) kbuf[c] = kread(c);
+#pragma unroll
+    for (int c = 0; c < F_CHUNKS; ++c) {
+      const f32x4 kv = kbuf[c % QK_AHEAD];
+      if (c + QK_AHEAD < F_CHUNKS) kbuf[c % QK_AHEAD] = kread(c + QK_AHEAD);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sacc[c & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[i], qf[c][i], sacc[c & 1], 0, 0, 0);
+      if (c == F_CHUNKS / 2 && more) gather(it + 2, sn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- scale, mask, online softmax (base 2); lane: row l16, keys 4 grp + i
+    const unsigned long long anc_row = anc_s[row_ok ? qrow / a.H : 0];
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kt + 4 * grp + i;
+      const int u = key - P;
+      const bool vis = (key < k1) & ((u < 0) | (((anc_row >> (u & 63)) & 1ull) != 0));
+      sv[i] = vis ? (sacc[0][i] + sacc[1][i]) * a.qk_scale_log2 : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool raise = mx > m_run + LAZY_RESCALE_LOG2;
+    const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
+    m_run = raise ? mx : m_run;
+    const float mu = m_run == -INFINITY ? 0.f : m_run;
+    float pw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pw[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
+    l_run = l_run * alpha + ((pw[0] + pw[1]) + (pw[2] + pw[3]));
+    if (__ballot(raise) != 0) {  // O (PV up to tile it-1) *= alpha
+      mfma_drain();
+#pragma unroll
+      for (int e = 0; e < F_PV_BLOCKS; ++e) acc_scale4(o[e], alpha);
+      mfma_valu_gap();
+    }
+    // ---- O^T += V^T P^T: 4 key steps x 32 feature blocks (consecutive MFMAs
+    // use different accumulators)
+    mfma_valu_gap();
+    uint32_t vb[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e3 = 0; e3 < 4; ++e3) vb[i][e3] = cur + v_off[i][e3];
+    auto vread = [&](int st) {  // step st = 32 i + e
+      const int i = st >> 5, e = st & 31;
+      return *(const LDS_AS float*)(uintptr_t)(vb[i][e & 3] + 256 * (e >> 2));
+    };
+    constexpr int V_AHEAD = 8;
+    float vbuf[V_AHEAD];
+#pragma unroll
+    for (int st = 0; st < V_AHEAD; ++st) vbuf[st] = vread(st);
+#pragma unroll
+    for (int st = 0; st < 4 * F_PV_BLOCKS; ++st) {
+      const float v = vbuf[st % V_AHEAD];
+      if (st + V_AHEAD < 4 * F_PV_BLOCKS) vbuf[st % V_AHEAD] = vread(st + V_AHEAD);
+      mfma16_acc(o[st & 31], v, pw[st >> 5]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmcnt<0>();
+  mfma_drain();
+
+  if (!wave_active) return;
+  // l: the four lane groups of a row hold disjoint keys
+  float l_row = l_run + __shfl_xor(l_run, 16);
+  l_row += __shfl_xor(l_row, 32);
+  if (row_ok) {
+    const int64_t rowid = (int64_t)g * a.M + qrow;
+    float* po = a.part_o + rowid * V_DIM + 4 * grp;
+#pragma unroll
+    for (int e = 0; e < F_PV_BLOCKS; ++e) *reinterpret_cast<f32x4*>(po + 16 * e) = o[e];
+    if (grp == 0) {
+      a.part_ml[2 * rowid] = m_run;
+      a.part_ml[2 * rowid + 1] = l_row;
+    }
+  }
+}
+
 // ------------------------------------------------------------ combine kernel
 // Output row (b, r) = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
 // sequence's splits s, M = max_s m_s, rounded to bf16 (nearest even).
@@ -773,7 +1067,7 @@ void verify_attn_partial_kernel(PartialArgs a) {
 // wave takes its splits COMBINE_BATCH at a time with every load of the batch
 // issued before the first use (one memory round trip per batch), keeping a
 // running maximum and rescaling its sums when the maximum rises.
-template <int WPR>
+template <int WPR, bool F32_OUT>
 __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_kernel(CombineArgs a) {
   constexpr int WAVES = WPR < 4 ? 4 : WPR;
   constexpr int ROWS = WAVES / WPR;
@@ -861,6 +1155,12 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
   }
   if (!active) return;
   const float inv = L > 0.f ? 1.0f / L : 0.f;
+  if constexpr (F32_OUT) {
+    float* dst = a.out_f32 + grow * V_DIM + 4 * lane;
+    *reinterpret_cast<f32x4*>(dst) = acc0 * inv;
+    *reinterpret_cast<f32x4*>(dst + 256) = acc1 * inv;
+    return;
+  }
   auto pack4 = [&](const f32x4& v) {
     uint2 p;
     p.x = (uint32_t)f32_to_bf16_rne(v[0] * inv) | ((uint32_t)f32_to_bf16_rne(v[1] * inv) << 16);
@@ -940,11 +1240,11 @@ int validate(const verify_attn_params* p) {
   return VERIFY_ATTN_OK;
 }
 
-int make_plan(const verify_attn_params* p, Plan* pl) {
+int make_plan(const verify_attn_params* p, Plan* pl, int rows_per_tile = ROWS_PER_TILE, int nk = NK) {
   const int rc = validate(p);
   if (rc) return rc;
   const int64_t M = (int64_t)p->num_heads * p->tree_size;
-  const int64_t row_tiles = ceil_div64(M, ROWS_PER_TILE);
+  const int64_t row_tiles = ceil_div64(M, rows_per_tile);
   int64_t chunk;
   if (p->nsplit > 0) {
     chunk = ceil_div64(p->max_seq_len, p->nsplit);
@@ -954,7 +1254,7 @@ int make_plan(const verify_attn_params* p, Plan* pl) {
     int64_t best = 0, best_cost = INT64_MAX;
     for (int64_t per_cu = 1; per_cu <= 4; per_cu *= 2) {
       int64_t c = ceil_div64(p->total_kv * row_tiles, NUM_CUS * per_cu);
-      c = ceil_div64(c < MIN_CHUNK ? MIN_CHUNK : c, NK) * NK;
+      c = ceil_div64(c < MIN_CHUNK ? MIN_CHUNK : c, nk) * nk;
       const int64_t items = (ceil_div64(p->total_kv, c) + p->num_seqs - 1) * row_tiles;
       const int64_t cost = ceil_div64(items, NUM_CUS) * c;
       if (cost < best_cost) {
@@ -964,8 +1264,8 @@ int make_plan(const verify_attn_params* p, Plan* pl) {
     }
     chunk = best;
   }
-  chunk = ceil_div64(chunk, NK) * NK;
-  const int64_t len_cap = ceil_div64(p->max_seq_len, NK) * NK;
+  chunk = ceil_div64(chunk, nk) * nk;
+  const int64_t len_cap = ceil_div64(p->max_seq_len, nk) * nk;
   if (chunk > len_cap) chunk = len_cap;
   const int64_t max_splits = ceil_div64(p->total_kv, chunk) + p->num_seqs;
   const int64_t blocks = ceil_div64(max_splits * row_tiles, 8) * 8;
@@ -1036,12 +1336,13 @@ int launch_partial(const verify_attn_params* p, const Plan& pl, const void* q, c
 }
 
 int launch_combine(const verify_attn_params* p, const Plan& pl, const int32_t* seq_lens, void* out,
-                   void* workspace, hipStream_t stream) {
+                   void* workspace, hipStream_t stream, bool f32_out = false) {
   CombineArgs a;
   a.part_o = static_cast<const float*>(workspace);
   a.part_ml = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + pl.part_o_bytes);
   a.seq_lens = seq_lens;
-  a.out = static_cast<uint16_t*>(out);
+  a.out = f32_out ? nullptr : static_cast<uint16_t*>(out);
+  a.out_f32 = f32_out ? static_cast<float*>(out) : nullptr;
   a.B = p->num_seqs;
   a.T = p->tree_size;
   a.M = pl.M;
@@ -1049,13 +1350,51 @@ int launch_combine(const verify_attn_params* p, const Plan& pl, const int32_t* s
   a.max_splits = pl.max_splits;
   a.max_seq_len = p->max_seq_len;
   const dim3 grid(pl.combine_blocks);
-  switch (pl.combine_wpr) {
-    case 16: hipLaunchKernelGGL(verify_attn_combine_kernel<16>, grid, dim3(16 * 64), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(verify_attn_combine_kernel<8>, grid, dim3(8 * 64), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(verify_attn_combine_kernel<4>, grid, dim3(4 * 64), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(verify_attn_combine_kernel<2>, grid, dim3(4 * 64), 0, stream, a); break;
-    default: hipLaunchKernelGGL(verify_attn_combine_kernel<1>, grid, dim3(4 * 64), 0, stream, a); break;
+#define VA_COMBINE(W, F) hipLaunchKernelGGL((verify_attn_combine_kernel<W, F>), grid, dim3((W < 4 ? 4 : W) * 64), 0, stream, a)
+  if (f32_out) {
+    switch (pl.combine_wpr) {
+      case 16: VA_COMBINE(16, true); break;
+      case 8: VA_COMBINE(8, true); break;
+      case 4: VA_COMBINE(4, true); break;
+      case 2: VA_COMBINE(2, true); break;
+      default: VA_COMBINE(1, true); break;
+    }
+  } else {
+    switch (pl.combine_wpr) {
+      case 16: VA_COMBINE(16, false); break;
+      case 8: VA_COMBINE(8, false); break;
+      case 4: VA_COMBINE(4, false); break;
+      case 2: VA_COMBINE(2, false); break;
+      default: VA_COMBINE(1, false); break;
+    }
   }
+#undef VA_COMBINE
+  return hipGetLastError() == hipSuccess ? VERIFY_ATTN_OK : VERIFY_ATTN_ERR_LAUNCH_FAILED;
+}
+
+int launch_partial_f32(const verify_attn_params* p, const Plan& pl, const float* q, const float* kv_pool,
+                       const int32_t* slot_idx, const int32_t* seq_lens, const int32_t* tree_parent,
+                       void* workspace, hipStream_t stream) {
+  PartialF32Args a;
+  a.q = q;
+  a.kv = kv_pool;
+  a.slot_idx = slot_idx;
+  a.seq_lens = seq_lens;
+  a.tree_parent = tree_parent;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_o_bytes);
+  a.B = p->num_seqs;
+  a.H = p->num_heads;
+  a.T = p->tree_size;
+  a.M = pl.M;
+  a.row_tiles = pl.row_tiles;
+  a.chunk = pl.chunk;
+  a.max_splits = pl.max_splits;
+  a.max_seq_len = p->max_seq_len;
+  a.total_kv = p->total_kv;
+  a.pool_slots = p->pool_slots;
+  a.qk_scale_log2 = p->sm_scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(verify_attn_f32_partial_kernel, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
   return hipGetLastError() == hipSuccess ? VERIFY_ATTN_OK : VERIFY_ATTN_ERR_LAUNCH_FAILED;
 }
 
@@ -1139,6 +1478,28 @@ int verify_attn(const verify_attn_params* p, const void* q, const void* kv_pool,
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if ((rc = launch_partial(p, pl, q, kv_pool, slot_idx, seq_lens, tree_parent, workspace, s))) return rc;
   return launch_combine(p, pl, seq_lens, out, workspace, s);
+}
+
+size_t verify_attn_f32_workspace_size(const verify_attn_params* p) {
+  Plan pl;
+  return make_plan(p, &pl, F_ROWS_PER_TILE, F_NK) == VERIFY_ATTN_OK ? pl.ws_bytes : 0;
+}
+
+int verify_attn_f32(const verify_attn_params* p, const float* q, const float* kv_pool, const int32_t* slot_idx,
+                    const int32_t* seq_lens, const int32_t* tree_parent, float* out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  Plan pl;
+  int rc = make_plan(p, &pl, F_ROWS_PER_TILE, F_NK);
+  if (rc) return rc;
+  if (!q || !kv_pool || !slot_idx || !seq_lens || !tree_parent || !out || !workspace) return VERIFY_ATTN_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out) || !aligned16(workspace)) return VERIFY_ATTN_ERR_MISALIGNED;
+  if (((uintptr_t)slot_idx & 3u) || ((uintptr_t)seq_lens & 3u) || ((uintptr_t)tree_parent & 3u))
+    return VERIFY_ATTN_ERR_MISALIGNED;
+  if (workspace_bytes < pl.ws_bytes) return VERIFY_ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if ((rc = check_device())) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((rc = launch_partial_f32(p, pl, q, kv_pool, slot_idx, seq_lens, tree_parent, workspace, s))) return rc;
+  return launch_combine(p, pl, seq_lens, out, workspace, s, true);
 }
 
 int verify_attn_append_kv(const verify_attn_params* p, const void* kv_new, const int32_t* slot_idx,

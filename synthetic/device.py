@@ -6,11 +6,18 @@ import numpy as np
 
 
 def to_device(wl, device="cuda"):
-    """torch tensors on `device`: bf16 q / kv_pool (from their bit patterns), int32 rest."""
+    """torch tensors on `device`: bf16 q / kv_pool (from their bit patterns) or
+    float32 ones for an fp32 workload, int32 rest."""
     import torch
+    if wl.q.dtype == np.float32:
+        q = torch.from_numpy(wl.q).to(device)
+        kv = torch.from_numpy(wl.kv_pool).to(device)
+    else:
+        q = torch.from_numpy(wl.q.view(np.int16)).view(torch.bfloat16).to(device)
+        kv = torch.from_numpy(wl.kv_pool.view(np.int16)).view(torch.bfloat16).to(device)
     return dict(
-        q=torch.from_numpy(wl.q.view(np.int16)).view(torch.bfloat16).to(device),
-        kv_pool=torch.from_numpy(wl.kv_pool.view(np.int16)).view(torch.bfloat16).to(device),
+        q=q,
+        kv_pool=kv,
         slot_idx=torch.from_numpy(wl.slot_idx).to(device),
         seq_lens=torch.from_numpy(wl.seq_lens).to(device),
         tree_parent=torch.from_numpy(wl.tree_parent).to(device),

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert mtv.verify_attn_version() == (1 << 16) | 2
+    assert mtv.verify_attn_version() == (1 << 16) | 3
 
 
 def base_params(**kw):
@@ -168,3 +168,25 @@ def test_compact_kv_errors(lib):
     import torch
     if torch.cuda.device_count() == 0:
         assert lib.verify_attn_compact_kv(ctypes.byref(p), *args, None) == header_enum("VERIFY_ATTN_ERR_DEVICE")
+
+
+def test_f32_entry_errors(lib):
+    """The fp32 entry point validates like the bf16 one and needs its own workspace size."""
+    p = base_params()
+    n32 = lib.verify_attn_f32_workspace_size(ctypes.byref(p))
+    assert n32 > 0
+    a = 1 << 20
+    args = [a, a, a, a, a, a, a]  # q, kv, slot, lens, parent, out, ws
+    for i in range(7):
+        bad = list(args)
+        bad[i] = None
+        assert lib.verify_attn_f32(ctypes.byref(p), *bad, n32, None) == header_enum("VERIFY_ATTN_ERR_NULL_PTR"), i
+    for i in (0, 1, 5, 6):
+        bad = list(args)
+        bad[i] = a + 8
+        assert lib.verify_attn_f32(ctypes.byref(p), *bad, n32, None) == header_enum("VERIFY_ATTN_ERR_MISALIGNED"), i
+    assert lib.verify_attn_f32(ctypes.byref(p), *args, n32 - 1, None) == header_enum(
+        "VERIFY_ATTN_ERR_WORKSPACE_TOO_SMALL")
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert lib.verify_attn_f32(ctypes.byref(p), *args, n32, None) == header_enum("VERIFY_ATTN_ERR_DEVICE")
