@@ -619,7 +619,10 @@ void verify_attn_partial_kernel(PartialArgs a) {
     } else if (st == 3) {
       mx = fmaxf(mx, xor32(mx));  // lanes l and l^32 hold the same query row
       const bool raise = mx > m_run + LAZY_RESCALE_LOG2;
-      any_raise = __ballot(raise) != 0;
+      // O needs rescaling only in rows that already hold weights: a row whose
+      // running max was -inf has O = 0 (its first finite max is the common case
+      // at the first tile of a split).
+      any_raise = __ballot(raise & (m_run != -INFINITY)) != 0;
       alpha = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;  // m_run = -inf -> 0
       m_run = raise ? mx : m_run;
       l_run *= alpha;
@@ -1001,6 +1004,7 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const bool raise = mx > m_run + LAZY_RESCALE_LOG2;
+    const bool rescale = __ballot(raise & (m_run != -INFINITY)) != 0;  // rows with weights so far
     const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
     m_run = raise ? mx : m_run;
     const float mu = m_run == -INFINITY ? 0.f : m_run;
@@ -1008,7 +1012,7 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) pw[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
     l_run = l_run * alpha + ((pw[0] + pw[1]) + (pw[2] + pw[3]));
-    if (__ballot(raise) != 0) {  // O (PV up to tile it-1) *= alpha
+    if (rescale) {  // O (PV up to tile it-1) *= alpha
       mfma_drain();
 #pragma unroll
       for (int e = 0; e < F_PV_BLOCKS; ++e) acc_scale4(o[e], alpha);
