@@ -110,6 +110,34 @@ def test_many_sequences(orc, B):
     check_full(orc, small(B=B, H=2, T=4, prefixes=prefixes, seed=B))
 
 
+@pytest.mark.parametrize("extra", [1, 700, 5000])
+def test_length_bound_above_actual(orc, extra):
+    """One sequence whose host-side bound max_seq_len exceeds its actual length:
+    the work items are dealt from the bound, splits past the end do nothing,
+    and the last split (40 keys here) re-reads its slot entries. The partial
+    results match those of the exact bound bit for bit (the combine's wave
+    count follows the bound, so only its merge order may differ), and the
+    output passes the oracle gate."""
+    import torch
+    import mla_tree_verify_latent_amd as mtv
+    wl = small(B=1, H=8, T=16, prefixes=[2072], seed=31)
+    dev = to_device(wl)
+    def partials(prm):
+        ws = torch.zeros(mtv.verify_attn_workspace_size(prm), dtype=torch.uint8, device="cuda")
+        mtv.verify_attn_partial(dev["q"], dev["kv_pool"], dev["slot_idx"], dev["seq_lens"],
+                                dev["tree_parent"], ws, prm)
+        torch.cuda.synchronize()
+        return ws.cpu().numpy()
+    prm = mtv.make_params(num_seqs=1, num_heads=wl.H, tree_size=wl.T, max_seq_len=wl.max_seq_len + extra,
+                          total_kv=wl.total_kv, pool_slots=wl.pool_slots, sm_scale=wl.sm_scale)
+    assert np.array_equal(partials(prm), partials(params_of(wl)))
+    out = mtv.VerifyAttention(prm)(**dev)
+    torch.cuda.synchronize()
+    got = bf16_out_to_f32(out)
+    ok, worst, idx = parity_gate(got, orc.run(wl))
+    assert ok, f"worst row {idx} at {worst:.2f} bf16 ulp"
+
+
 @pytest.mark.parametrize("tree", ["flat", "chain"])
 def test_tree_shapes(orc, tree):
     check_full(orc, small(H=4, T=64, prefixes=[300], tree=tree, seed=5))
