@@ -57,7 +57,47 @@ def check_registers(extra=()) -> dict:
         p = found[0]
         if p["vgpr_spill"] or p["sgpr_spill"] or not agpr_ok(p["agpr"]):
             raise RuntimeError(f"{kname} register allocation changed: {p}")
+    check_mfma_hazards(text, "verify_attn_f32_partial_kernel")
     return info
+
+
+def _vregs(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]$", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def check_mfma_hazards(text, kernel):
+    """The asm MFMAs of `kernel` that accumulate in AGPRs carry no wait states
+    of their own: require that none of the two instructions issued before one
+    of them is a VALU instruction writing one of its source VGPRs."""
+    start = text.index(kernel)
+    body = text[text.index(":", text.index("\n" + "_Z", start - 200) + 1):]
+    body = body[:body.index("s_endpgm")]
+    ins = [l.split(";")[0].strip() for l in body.splitlines()]
+    ins = [l for l in ins if l and not l.startswith(".") and not l.endswith(":")]
+    for i, line in enumerate(ins):
+        if not (line.startswith("v_mfma") and " a[" in line):
+            continue
+        ops = [t.strip() for t in line.split(None, 1)[1].split(",")]
+        src = _vregs(ops[1]) | _vregs(ops[2])
+        issued, k = 0, i - 1
+        while k >= 0 and issued < 2:
+            prev = ins[k]
+            k -= 1
+            if prev.startswith("s_nop"):
+                issued += int(prev.split()[1]) + 1
+                continue
+            if prev.startswith("s_waitcnt"):
+                continue
+            issued += 1
+            if prev.startswith("v_") and not prev.startswith("v_mfma"):
+                dst = _vregs(prev.split(None, 1)[1].split(",")[0].strip())
+                if dst & src:
+                    raise RuntimeError(f"{kernel}: VALU write right before an asm MFMA source: "
+                                       f"{prev!r} -> {line!r}")
 
 
 def build(out: str = LIB, extra=()) -> str:

@@ -824,8 +824,12 @@ struct PartialF32Args {
   float qk_scale_log2;
 };
 
+// acc += a * b (MFMA 16x16x4 f32) on an AGPR accumulator. No wait states in
+// front: in the fp32 kernel's PV loop A comes straight from an LDS read and B
+// was written by VALU before a mfma_valu_gap(); build.py checks the generated
+// code for a VALU write to a source of these MFMAs just before them.
 __device__ __forceinline__ void mfma16_acc(f32x4& acc, float a, float b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x4_f32 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void acc_scale4(f32x4& acc, float s) {
 #pragma unroll
@@ -977,13 +981,14 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
 #pragma unroll
     for (int c3 = 0; c3 < 4; ++c3) kb[c3] = cur + k_off[c3];
     auto kread = [&](int c) { return *(const LDS_AS f32x4*)(uintptr_t)(kb[c & 3] + 256 * (c >> 2)); };
-    f32x4 kbuf[QK_AHEAD];
+    constexpr int FK_AHEAD = 6;  // K reads in flight
+    f32x4 kbuf[FK_AHEAD];
 #pragma unroll
-    for (int c = 0; c < QK_AHEAD; ++c) kbuf[c] = kread(c);
+    for (int c = 0; c < FK_AHEAD; ++c) kbuf[c] = kread(c);
 #pragma unroll
     for (int c = 0; c < F_CHUNKS; ++c) {
-      const f32x4 kv = kbuf[c % QK_AHEAD];
-      if (c + QK_AHEAD < F_CHUNKS) kbuf[c % QK_AHEAD] = kread(c + QK_AHEAD);
+      const f32x4 kv = kbuf[c % FK_AHEAD];
+      if (c + FK_AHEAD < F_CHUNKS) kbuf[c % FK_AHEAD] = kread(c + FK_AHEAD);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         sacc[c & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[i], qf[c][i], sacc[c & 1], 0, 0, 0);
@@ -1030,7 +1035,7 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
       const int i = st >> 5, e = st & 31;
       return *(const LDS_AS float*)(uintptr_t)(vb[i][e & 3] + 256 * (e >> 2));
     };
-    constexpr int V_AHEAD = 8;
+    constexpr int V_AHEAD = 16;
     float vbuf[V_AHEAD];
 #pragma unroll
     for (int st = 0; st < V_AHEAD; ++st) vbuf[st] = vread(st);
