@@ -78,6 +78,7 @@ struct Plan {
   int max_splits;      // bound on the total number of splits
   int partial_blocks;  // multiple of 8
   int combine_wpr;     // waves per output row in the combine kernel (1, 2, 4, 8 or 16)
+  int combine_halves;  // workgroups per row group (2: one per half of the features)
   int combine_blocks;
   size_t part_o_bytes;
   size_t ws_bytes;
@@ -1076,7 +1077,7 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
 // wave takes its splits COMBINE_BATCH at a time with every load of the batch
 // issued before the first use (one memory round trip per batch), keeping a
 // running maximum and rescaling its sums when the maximum rises.
-template <int WPR, bool F32_OUT>
+template <int WPR, bool F32_OUT, bool HALF = false>
 __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_kernel(CombineArgs a) {
   constexpr int WAVES = WPR < 4 ? 4 : WPR;
   constexpr int ROWS = WAVES / WPR;
@@ -1087,7 +1088,9 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int sub = wave % WPR;
-  const int64_t grow = (int64_t)blockIdx.x * ROWS + wave / WPR;
+  // HALF: two workgroups per row group, one per half of the 512 features.
+  const int64_t grow = (int64_t)(HALF ? blockIdx.x >> 1 : blockIdx.x) * ROWS + wave / WPR;
+  const int foff = (HALF ? (blockIdx.x & 1) * 256 : 0) + 4 * lane;  // first feature of this lane
   const bool active = grow < (int64_t)a.B * a.M;
   const int b = active ? (int)(grow / a.M) : 0;
   const int row = active ? (int)(grow - (int64_t)b * a.M) : 0;
@@ -1116,9 +1119,9 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
         const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * rowid);
         m[j] = ml[0];
         l[j] = ml[1];
-        const float* src = a.part_o + rowid * V_DIM + 4 * lane;
+        const float* src = a.part_o + rowid * V_DIM + foff;
         o0[j] = *reinterpret_cast<const f32x4*>(src);
-        o1[j] = *reinterpret_cast<const f32x4*>(src + 256);
+        if (!HALF) o1[j] = *reinterpret_cast<const f32x4*>(src + 256);
       }
     }
     float mb = mloc;
@@ -1165,9 +1168,9 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
   if (!active) return;
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   if constexpr (F32_OUT) {
-    float* dst = a.out_f32 + grow * V_DIM + 4 * lane;
+    float* dst = a.out_f32 + grow * V_DIM + foff;
     *reinterpret_cast<f32x4*>(dst) = acc0 * inv;
-    *reinterpret_cast<f32x4*>(dst + 256) = acc1 * inv;
+    if (!HALF) *reinterpret_cast<f32x4*>(dst + 256) = acc1 * inv;
     return;
   }
   auto pack4 = [&](const f32x4& v) {
@@ -1176,9 +1179,9 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
     p.y = (uint32_t)f32_to_bf16_rne(v[2] * inv) | ((uint32_t)f32_to_bf16_rne(v[3] * inv) << 16);
     return p;
   };
-  uint16_t* dst = a.out + grow * V_DIM + 4 * lane;
+  uint16_t* dst = a.out + grow * V_DIM + foff;
   *reinterpret_cast<uint2*>(dst) = pack4(acc0);
-  *reinterpret_cast<uint2*>(dst + 256) = pack4(acc1);
+  if (!HALF) *reinterpret_cast<uint2*>(dst + 256) = pack4(acc1);
 }
 
 // ------------------------------------------------------------ append kernel
@@ -1285,7 +1288,10 @@ int make_plan(const verify_attn_params* p, Plan* pl, int rows_per_tile = ROWS_PE
   const int64_t seq_splits = ceil_div64(p->max_seq_len, chunk);
   int wpr = 1;
   while (wpr < 16 && rows * wpr * 2 <= COMBINE_WAVES && wpr * 2 <= seq_splits) wpr *= 2;
-  const int64_t cblocks = ceil_div64(rows, (wpr < 4 ? 4 : wpr) / wpr);
+  // Few rows: split the features of a row over two workgroups, so that more
+  // CUs read the partials.
+  const int halves = (wpr == 16 && rows * 16 * 2 <= COMBINE_WAVES) ? 2 : 1;
+  const int64_t cblocks = ceil_div64(rows, (wpr < 4 ? 4 : wpr) / wpr) * halves;
   if (blocks > INT32_MAX || cblocks > INT32_MAX || max_splits > INT32_MAX) return VERIFY_ATTN_ERR_BAD_DIM;
   pl->M = (int)M;
   pl->row_tiles = (int)row_tiles;
@@ -1293,6 +1299,7 @@ int make_plan(const verify_attn_params* p, Plan* pl, int rows_per_tile = ROWS_PE
   pl->max_splits = (int)max_splits;
   pl->partial_blocks = (int)blocks;
   pl->combine_wpr = wpr;
+  pl->combine_halves = halves;
   pl->combine_blocks = (int)cblocks;
   pl->part_o_bytes = (size_t)max_splits * (size_t)M * V_DIM * sizeof(float);
   pl->ws_bytes = pl->part_o_bytes + (size_t)max_splits * (size_t)M * 2 * sizeof(float);
@@ -1361,7 +1368,8 @@ int launch_combine(const verify_attn_params* p, const Plan& pl, const int32_t* s
   const dim3 grid(pl.combine_blocks);
 #define VA_COMBINE(W, F) hipLaunchKernelGGL((verify_attn_combine_kernel<W, F>), grid, dim3((W < 4 ? 4 : W) * 64), 0, stream, a)
   if (f32_out) {
-    switch (pl.combine_wpr) {
+    if (pl.combine_halves == 2) hipLaunchKernelGGL((verify_attn_combine_kernel<16, true, true>), grid, dim3(16 * 64), 0, stream, a);
+    else switch (pl.combine_wpr) {
       case 16: VA_COMBINE(16, true); break;
       case 8: VA_COMBINE(8, true); break;
       case 4: VA_COMBINE(4, true); break;
@@ -1369,7 +1377,8 @@ int launch_combine(const verify_attn_params* p, const Plan& pl, const int32_t* s
       default: VA_COMBINE(1, true); break;
     }
   } else {
-    switch (pl.combine_wpr) {
+    if (pl.combine_halves == 2) hipLaunchKernelGGL((verify_attn_combine_kernel<16, false, true>), grid, dim3(16 * 64), 0, stream, a);
+    else switch (pl.combine_wpr) {
       case 16: VA_COMBINE(16, false); break;
       case 8: VA_COMBINE(8, false); break;
       case 4: VA_COMBINE(4, false); break;
