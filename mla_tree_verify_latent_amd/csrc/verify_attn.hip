@@ -376,6 +376,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // LDS: a ring of 4 KV tiles of 32 rows (36 KB each). KV row k (0..31) of a
 // tile, 16-byte chunk c (0..71) of that row lives at
 //   (c / 8) * 4096 + k * 128 + ((c % 8) ^ swz(k)) * 16.
+// (In the prologue, the buffers of tiles 2 and 3 first stage the query.)
 // Every wave gathers 8 rows of each tile: wave w loads KV rows 8w..8w+7 with 9
 // direct-to-LDS loads of 1 KB (one per chunk group), lane -> (row 8w + lane/8,
 // chunk position lane%8), spread over its QK MFMAs. The slot-table entries of
