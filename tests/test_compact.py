@@ -114,3 +114,41 @@ def test_compact_then_verify_long_context_scattered():
     """The 64k-token scattered workload: verify after compaction gives the
     same bits as verify on the scattered pool."""
     _compact_then_verify_matches(inputs.config("c4a_long_scattered"))
+
+
+@pytest.mark.gpu
+def test_compact_then_verify_in_one_graph():
+    """Compaction and verify on the compacted rows recorded in one HIP graph:
+    every replay gives the bits of verify on the scattered pool."""
+    import torch
+    import mla_tree_verify_latent_amd as mtv
+    from synthetic.device import to_device, params_of
+    wl = inputs.make_workload("compact_graph", B=2, H=8, T=16, prefixes=[900, 2100], pool_slots=8192,
+                              seed=45)
+    dev = to_device(wl)
+    prm = params_of(wl)
+    ref = torch.empty((wl.B, wl.T, wl.H, 512), dtype=torch.bfloat16, device="cuda")
+    mtv.VerifyAttention(prm)(**dev, out=ref)
+    prm_c = mtv.make_params(num_seqs=wl.B, num_heads=wl.H, tree_size=wl.T, max_seq_len=wl.max_seq_len,
+                            total_kv=wl.total_kv, pool_slots=wl.total_kv, sm_scale=wl.sm_scale,
+                            page_size=64)
+    dst = torch.empty((wl.total_kv, 576), dtype=torch.bfloat16, device="cuda")
+    ident = torch.arange(wl.total_kv, dtype=torch.int32, device="cuda")
+    op = mtv.VerifyAttention(prm_c)
+    out = torch.empty_like(ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            mtv.verify_attn_compact_kv(dev["kv_pool"], dev["slot_idx"], dst, prm, stream=s)
+            op(q=dev["q"], kv_pool=dst, slot_idx=ident, seq_lens=dev["seq_lens"],
+               tree_parent=dev["tree_parent"], out=out, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        dst.zero_()
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"

@@ -118,3 +118,32 @@ def test_f32_long_context_sampled(orc):
     ok, worst, idx = rel_gate(g, ref)
     print(f"f32 long: worst sampled row {tuple(rows[idx])} rel err {worst:.3e}")
     assert ok, f"row {tuple(rows[idx])}: relative error {worst:.3e}"
+
+
+@pytest.mark.gpu
+def test_f32_graph_capture_replay():
+    """The fp32 call captured in a HIP graph: every replay (with eager work in
+    between) gives the eager call's bits."""
+    import torch
+    import mla_tree_verify_latent_amd as mtv
+    from synthetic.device import params_of, to_device
+    wl = f32_workload(B=2, H=8, T=16, prefixes=[1500, 300], seed=25)
+    dev = to_device(wl)
+    prm = params_of(wl)
+    ws = torch.empty(mtv.verify_attn_f32_workspace_size(prm), dtype=torch.uint8, device="cuda")
+    eager = run_gpu_f32(wl, dev=dev)
+    out = torch.empty((wl.B, wl.T, wl.H, 512), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            mtv.verify_attn_f32(dev["q"], dev["kv_pool"], dev["slot_idx"], dev["seq_lens"],
+                                dev["tree_parent"], out, ws, prm, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        out.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager), f"replay {rep}"
