@@ -203,14 +203,32 @@ int verify_attn_f32(const verify_attn_params* p, const float* q, const float* kv
 int verify_attn_compact_kv(const verify_attn_params* p, const void* kv_pool, const int32_t* slot_idx,
                            void* kv_dst, void* stream);
 
+/*
+ * Debug check of the device-resident inputs that the other entry points take
+ * as a precondition (for tests and bring-up, not for the hot path): enqueues
+ * a clear of *flags and a scan that sets
+ *   VERIFY_ATTN_BAD_LENGTH  some seq_lens[b] outside [tree_size, max_seq_len]
+ *   VERIFY_ATTN_BAD_TOTAL   sum of seq_lens > total_kv
+ *   VERIFY_ATTN_BAD_PARENT  some tree_parent[b][t] outside [-1, t-1]
+ *   VERIFY_ATTN_BAD_SLOT    some slot_idx[i] (i < total_kv) outside [0, pool_slots)
+ * flags: one int32 in device memory (caller-owned; read it after the stream
+ * has run). No allocation or host synchronisation. Status codes as above.
+ */
+#define VERIFY_ATTN_BAD_LENGTH 1
+#define VERIFY_ATTN_BAD_TOTAL 2
+#define VERIFY_ATTN_BAD_PARENT 4
+#define VERIFY_ATTN_BAD_SLOT 8
+int verify_attn_debug_validate(const verify_attn_params* p, const int32_t* slot_idx, const int32_t* seq_lens,
+                               const int32_t* tree_parent, int32_t* flags, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* verify_attn_strerror(int status);
 
 /* ABI version of this header: (major << 16) | minor (minor 1: verify_attn_append_kv; 2: verify_attn_compact_kv;
-   3: verify_attn_f32). */
+   3: verify_attn_f32; 4: verify_attn_debug_validate). */
 int verify_attn_version(void);
 
-#define VERIFY_ATTN_VERSION ((1 << 16) | 3)
+#define VERIFY_ATTN_VERSION ((1 << 16) | 4)
 
 #ifdef __cplusplus
 }

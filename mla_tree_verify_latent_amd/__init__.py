@@ -9,7 +9,7 @@ raise.
 Entry points mirror the C ABI declared in ``include/verify_attn.h``:
 ``verify_attn``, ``verify_attn_partial``, ``verify_attn_combine``,
 ``verify_attn_append_kv``, ``verify_attn_compact_kv``, ``verify_attn_f32``,
-``verify_attn_f32_workspace_size``, ``verify_attn_workspace_size``, ``verify_attn_plan``,
+``verify_attn_f32_workspace_size``, ``verify_attn_debug_validate``, ``verify_attn_workspace_size``, ``verify_attn_plan``,
 ``verify_attn_strerror``, ``verify_attn_version``.
 """
 from __future__ import annotations
@@ -28,6 +28,7 @@ MAX_TREE = 64
 EXPORTS = (
     "verify_attn", "verify_attn_partial", "verify_attn_combine", "verify_attn_append_kv",
     "verify_attn_compact_kv", "verify_attn_f32", "verify_attn_f32_workspace_size",
+    "verify_attn_debug_validate",
     "verify_attn_workspace_size",
     "verify_attn_plan", "verify_attn_strerror", "verify_attn_version",
 )
@@ -79,6 +80,8 @@ def load_library(path: str = LIB_PATH):
     lib.verify_attn.restype = ctypes.c_int
     lib.verify_attn_f32.argtypes = [P, vp, vp, i32p, i32p, i32p, vp, vp, ctypes.c_size_t, vp]
     lib.verify_attn_f32.restype = ctypes.c_int
+    lib.verify_attn_debug_validate.argtypes = [P, i32p, i32p, i32p, vp, vp]
+    lib.verify_attn_debug_validate.restype = ctypes.c_int
     lib.verify_attn_f32_workspace_size.argtypes = [P]
     lib.verify_attn_f32_workspace_size.restype = ctypes.c_size_t
     lib.verify_attn_partial.argtypes = [P, vp, vp, i32p, i32p, i32p, vp, ctypes.c_size_t, vp]
@@ -202,6 +205,23 @@ def verify_attn_f32(q, kv_pool, slot_idx, seq_lens, tree_parent, out, workspace,
         ctypes.byref(params), _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
         _ptr(tree_parent), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+# Bits of verify_attn_debug_validate's result
+BAD_LENGTH, BAD_TOTAL, BAD_PARENT, BAD_SLOT = 1, 2, 4, 8
+
+
+def verify_attn_debug_validate(slot_idx, seq_lens, tree_parent, params: Params, flags=None,
+                               stream=None) -> int:
+    """Check the device-resident inputs; returns the BAD_* bits (0 = valid).
+    Debug only: reads the result back (synchronises the stream)."""
+    import torch
+    if flags is None:
+        flags = torch.empty(1, dtype=torch.int32, device=slot_idx.device)
+    _check(load_library().verify_attn_debug_validate(
+        ctypes.byref(params), _ptr(slot_idx), _ptr(seq_lens), _ptr(tree_parent), _ptr(flags),
+        _stream(stream)))
+    return int(flags.item())
 
 
 def verify_attn_partial(q, kv_pool, slot_idx, seq_lens, tree_parent, workspace, params: Params,

@@ -27,6 +27,7 @@
 //  - a log-sum-exp combine kernel merges the splits and rounds to bf16.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -1231,6 +1232,50 @@ __global__ __launch_bounds__(256) void verify_attn_compact_kernel(CompactArgs a)
   if (lane < 8) dst[64 + lane] = v1;
 }
 
+// ------------------------------------------------------------ validation
+// Debug check of the device-resident inputs (not on the hot path): bits of
+// *flags are set for lengths outside [T, max_seq_len], lengths that add up to
+// more than total_kv, parents outside [-1, t-1], slots outside the pool.
+struct ValidateArgs {
+  const int32_t* slot_idx;
+  const int32_t* seq_lens;
+  const int32_t* tree_parent;
+  int32_t* flags;
+  int B, T, max_seq_len;
+  int64_t total_kv, pool_slots;
+};
+
+__global__ __launch_bounds__(64) void verify_attn_validate_clear(int32_t* flags) {
+  if (threadIdx.x == 0) *flags = 0;
+}
+
+__global__ __launch_bounds__(256) void verify_attn_validate_kernel(ValidateArgs a) {
+  int bits = 0;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nthreads = (int64_t)gridDim.x * 256;
+  if (blockIdx.x == 0 && threadIdx.x < 64) {  // lengths and their sum: one wave
+    long long sum = 0;
+    for (int b = threadIdx.x; b < a.B; b += 64) {
+      const int n = a.seq_lens[b];
+      if (n < a.T || n > a.max_seq_len) bits |= VERIFY_ATTN_BAD_LENGTH;
+      sum += n;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d);
+    if (sum > a.total_kv) bits |= VERIFY_ATTN_BAD_TOTAL;
+  }
+  for (int64_t i = gid; i < (int64_t)a.B * a.T; i += nthreads) {
+    const int t = (int)(i % a.T);
+    const int p = a.tree_parent[i];
+    if (p < -1 || p >= t) bits |= VERIFY_ATTN_BAD_PARENT;
+  }
+  for (int64_t i = gid; i < a.total_kv; i += nthreads) {
+    const int slot = a.slot_idx[i];
+    if (slot < 0 || (int64_t)slot >= a.pool_slots) bits |= VERIFY_ATTN_BAD_SLOT;
+  }
+  if (bits) atomicOr(a.flags, bits);
+}
+
 // ------------------------------------------------------------------- host
 
 constexpr int NUM_CUS = 256;        // MI355X compute units (one partial workgroup each)
@@ -1561,6 +1606,32 @@ int verify_attn_compact_kv(const verify_attn_params* p, const void* kv_pool, con
   if (ceil_div64(a.total_kv, 4) > INT32_MAX) return VERIFY_ATTN_ERR_BAD_DIM;
   hipLaunchKernelGGL(verify_attn_compact_kernel, dim3((unsigned)ceil_div64(a.total_kv, 4)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? VERIFY_ATTN_OK : VERIFY_ATTN_ERR_LAUNCH_FAILED;
+}
+
+int verify_attn_debug_validate(const verify_attn_params* p, const int32_t* slot_idx, const int32_t* seq_lens,
+                               const int32_t* tree_parent, int32_t* flags, void* stream) {
+  int rc = validate(p);
+  if (rc) return rc;
+  if (!slot_idx || !seq_lens || !tree_parent || !flags) return VERIFY_ATTN_ERR_NULL_PTR;
+  if (((uintptr_t)slot_idx & 3u) || ((uintptr_t)seq_lens & 3u) || ((uintptr_t)tree_parent & 3u) ||
+      ((uintptr_t)flags & 3u))
+    return VERIFY_ATTN_ERR_MISALIGNED;
+  if ((rc = check_device())) return rc;
+  ValidateArgs a;
+  a.slot_idx = slot_idx;
+  a.seq_lens = seq_lens;
+  a.tree_parent = tree_parent;
+  a.flags = flags;
+  a.B = p->num_seqs;
+  a.T = p->tree_size;
+  a.max_seq_len = p->max_seq_len;
+  a.total_kv = p->total_kv;
+  a.pool_slots = p->pool_slots;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(verify_attn_validate_clear, dim3(1), dim3(64), 0, s, flags);
+  const int64_t blocks = std::min<int64_t>(1024, ceil_div64(std::max<int64_t>(a.total_kv, (int64_t)a.B * a.T), 256));
+  hipLaunchKernelGGL(verify_attn_validate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? VERIFY_ATTN_OK : VERIFY_ATTN_ERR_LAUNCH_FAILED;
 }
 

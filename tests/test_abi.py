@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert mtv.verify_attn_version() == (1 << 16) | 3
+    assert mtv.verify_attn_version() == (1 << 16) | 4
 
 
 def base_params(**kw):
@@ -190,3 +190,20 @@ def test_f32_entry_errors(lib):
     import torch
     if torch.cuda.device_count() == 0:
         assert lib.verify_attn_f32(ctypes.byref(p), *args, n32, None) == header_enum("VERIFY_ATTN_ERR_DEVICE")
+
+
+def test_debug_validate_errors(lib):
+    p = base_params()
+    a = 1 << 20
+    args = [a, a, a, a]  # slot_idx, seq_lens, tree_parent, flags
+    for i in range(4):
+        bad = list(args)
+        bad[i] = None
+        assert lib.verify_attn_debug_validate(ctypes.byref(p), *bad, None) == header_enum("VERIFY_ATTN_ERR_NULL_PTR"), i
+    for i in range(4):
+        bad = list(args)
+        bad[i] = a + 2
+        assert lib.verify_attn_debug_validate(ctypes.byref(p), *bad, None) == header_enum("VERIFY_ATTN_ERR_MISALIGNED"), i
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert lib.verify_attn_debug_validate(ctypes.byref(p), *args, None) == header_enum("VERIFY_ATTN_ERR_DEVICE")
