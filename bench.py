@@ -194,9 +194,17 @@ def cpu_baseline(name, repeats=3):
         orc.run(wl)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": algorithmic_bytes(wl) / t / 1e9, "unit": "GB/s", "cores": orc.num_threads(),
-        "kind": "oracle",
+        "kind": "oracle", "cpu_model": model, "nproc": os.cpu_count(),
         "sample": f"{name}: whole call ({wl.B * wl.T * wl.H} output rows), median of {repeats} "
                   f"calls, {t:.2f} s per call",
         "s_per_call": t,
@@ -375,10 +383,17 @@ def main():
             "plan": head["plan"], "replicas": head["replicas"],
         },
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        # whole call against the binding roof: max(bytes at 8 TB/s, flops at 2.5 PFLOP/s) / time
+        "binding_roof_frac": round(max(head["bytes"] / (HBM_PEAK_GBS * 1e9),
+                                       head["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3), 4),
+        "ms_per_step_repeats": [round(x, 5) for x in head["full_ms_repeats"]],
         "calls_per_s": round(1e3 / ms, 1),
         "ms_per_call_mall_warm": round(head["full_ms_mall_warm"], 5),
         "partial_kernel_ms": round(part_ms, 5),
         "combine_share": round(1.0 - part_ms / ms, 4),
+        # measured HBM bytes of the partial kernel (rocprofv3 counters) over its live time
+        "partial_hbm_gbs": (round(traffic_from_counters(part_ms) / (part_ms * 1e-3) / 1e9, 1)
+                            if traffic_from_counters(part_ms) else None),
         "roofline": {
             "bound": "mfma",
             "achieved": round(part_tflops, 1),
