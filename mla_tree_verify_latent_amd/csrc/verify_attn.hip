@@ -1281,6 +1281,7 @@ __global__ __launch_bounds__(256) void verify_attn_validate_kernel(ValidateArgs 
 constexpr int NUM_CUS = 256;        // MI355X compute units (one partial workgroup each)
 constexpr int MIN_CHUNK = 256;      // keys per split below which partials dominate
 constexpr int64_t COMBINE_WAVES = 4096;  // combine waves resident at once (16 per CU)
+constexpr int64_t ROUND_COST_TILES = 4;  // fixed cost of a round of workgroups, in tiles
 
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -1307,14 +1308,19 @@ int make_plan(const verify_attn_params* p, Plan* pl, int rows_per_tile = ROWS_PE
   if (p->nsplit > 0) {
     chunk = ceil_div64(p->max_seq_len, p->nsplit);
   } else {
-    // Fewest full rounds of one workgroup per CU: try 1, 2 and 4 workgroups per
-    // CU and keep the split length with the smallest (rounds x keys per split).
+    // Try 1, 2, 4, 8 and 16 workgroups per CU and keep the split length with the
+    // lowest estimated time, in units of one tile of nk keys: every round of one
+    // workgroup per CU costs its tiles plus a fixed start and end (about four
+    // tiles: first loads, partial store), and every (split, row tile) item
+    // about a twentieth of a tile of partial traffic (written, then read by
+    // the combine). More, shorter splits fill the last round better but add
+    // fixed costs and partials.
     int64_t best = 0, best_cost = INT64_MAX;
-    for (int64_t per_cu = 1; per_cu <= 4; per_cu *= 2) {
+    for (int64_t per_cu = 1; per_cu <= 16; per_cu *= 2) {
       int64_t c = ceil_div64(p->total_kv * row_tiles, NUM_CUS * per_cu);
       c = ceil_div64(c < MIN_CHUNK ? MIN_CHUNK : c, nk) * nk;
       const int64_t items = (ceil_div64(p->total_kv, c) + p->num_seqs - 1) * row_tiles;
-      const int64_t cost = ceil_div64(items, NUM_CUS) * c;
+      const int64_t cost = ceil_div64(items, NUM_CUS) * (20 * (c / nk) + 20 * ROUND_COST_TILES) + items;
       if (cost < best_cost) {
         best_cost = cost;
         best = c;
