@@ -508,7 +508,9 @@ void verify_attn_partial_kernel(PartialArgs a) {
       qf[half * (QK_STEPS / 2) + k] = __builtin_bit_cast(bf16x8, v);
     }
   };
-  q_stage(0);
+  // A wave without query rows skips the staging loads (its reads are then
+  // replaced by zeros above; the waits below only get looser).
+  if (wave_active) q_stage(0);
 
   // Steady-state load order (iteration i: slots of tile i+5, gather of tile
   // i+3) for i = -3, -2: the gathers of tiles 0 and 1. Forming their row
@@ -528,7 +530,7 @@ void verify_attn_partial_kernel(PartialArgs a) {
   q_read(0);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 7, 0));  // read out before the second half lands
   asm volatile("" ::: "memory");
-  q_stage(1);
+  if (wave_active) q_stage(1);
   wait_vmcnt<0>();  // second query half, and with it tiles 0 and 1, landed
   asm volatile("" ::: "memory");
   q_read(1);
