@@ -483,16 +483,18 @@ void verify_attn_partial_kernel(PartialArgs a) {
   // tiles 2 and 3, which are free until the QK of tile 0. Read straight into
   // the MFMA layout, each load instruction would touch 32 rows; staged, each
   // direct-to-LDS load reads 1 KB of consecutive query bytes. Staging slot
-  // s = 36 r + p' holds piece p' ^ ((r >> 1) & 3) of row r (a permutation
-  // inside aligned groups of four pieces), so that the MFMA-layout reads of
-  // eight consecutive rows fall on eight distinct 16-byte positions.
+  // s = 36 r + p' holds piece p' ^ qswz(r) of row r (a permutation inside
+  // aligned groups of four pieces), so that the MFMA-layout reads of eight
+  // consecutive rows fall on eight distinct 16-byte positions and rows r and
+  // r + 16 on positions that differ in bit 0 (the rules of swz above).
   const uint32_t qstage = smem_base + 2 * TILE_BYTES + wave * QSTAGE_BYTES;
+  auto qswz = [](int r) { return ((r >> 1) & 3) ^ ((r >> 4) & 1); };
   auto q_stage = [&](int half) {
 #pragma unroll
     for (int j = 0; j < QSTAGE_LOADS; ++j) {
       const int slot = j * 64 + lane;
       const int r = slot / QSTAGE_PIECES;
-      const int p = (slot - r * QSTAGE_PIECES) ^ ((r >> 1) & 3);
+      const int p = (slot - r * QSTAGE_PIECES) ^ qswz(r);
       const int grow = row0 + r < a.M ? row0 + r : 0;  // rows past M read row 0
       load_to_lds16(a.q + ((int64_t)loc.b * a.M + grow) * KV_DIM + half * (KV_DIM / 2) + 8 * p,
                     qstage + j * 1024);
@@ -503,7 +505,7 @@ void verify_attn_partial_kernel(PartialArgs a) {
 #pragma unroll
     for (int k = 0; k < QK_STEPS / 2; ++k) {
       const int p = 2 * k + hl;
-      u32x4 v = __builtin_bit_cast(u32x4, lds_read_b128(qstage + (r * QSTAGE_PIECES + (p ^ ((r >> 1) & 3))) * 16));
+      u32x4 v = __builtin_bit_cast(u32x4, lds_read_b128(qstage + (r * QSTAGE_PIECES + (p ^ qswz(r))) * 16));
       if (!row_ok) v = u32x4{0u, 0u, 0u, 0u};
       qf[half * (QK_STEPS / 2) + k] = __builtin_bit_cast(bf16x8, v);
     }
