@@ -222,6 +222,16 @@ def traffic_from_counters(partial_ms):
     return c["hbm_bytes_per_launch"]
 
 
+def counter_value(key):
+    """One figure of the committed counter summary, if taken on this source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    c = json.load(open(COUNTERS_FILE))
+    if c.get("kernel_source_sha256_16") != kernel_source_digest() or key not in c:
+        return None
+    return round(c[key], 4)
+
+
 def _read_counter_csv(path, kernel_substr):
     import csv
     vals = {}
@@ -264,6 +274,12 @@ def summarize(args):
         "hbm_read_bytes_per_launch": fb, "hbm_write_bytes_per_launch": wb,
         "hbm_bytes_per_launch": fb + wb,
     }
+    if args.sq:
+        # SQ counters of the same kernel: MFMA busy cycles (summed over the 1,024
+        # SIMDs) over GRBM_GUI_ACTIVE (summed over the 8 XCDs) -> busy fraction
+        sq, _ = _read_counter_csv(args.sq, "verify_attn_partial")
+        out["mfma_busy_frac"] = sq["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / (sq["GRBM_GUI_ACTIVE"] / 8)
+        out["lds_bank_conflict_cycles"] = sq["SQ_LDS_BANK_CONFLICT"]
     print(json.dumps(out, indent=1))
 
 
@@ -288,6 +304,7 @@ def main():
     ap.add_argument("--write")
     ap.add_argument("--copy-fetch")
     ap.add_argument("--copy-write")
+    ap.add_argument("--sq", help="SQ/GRBM counter file of the same kernel (MFMA busy)")
     args = ap.parse_args()
     if args.summarize:
         summarize(args)
@@ -394,6 +411,7 @@ def main():
         # measured HBM bytes of the partial kernel (rocprofv3 counters) over its live time
         "partial_hbm_gbs": (round(traffic_from_counters(part_ms) / (part_ms * 1e-3) / 1e9, 1)
                             if traffic_from_counters(part_ms) else None),
+        "partial_mfma_busy": counter_value("mfma_busy_frac"),
         "roofline": {
             "bound": "mfma",
             "achieved": round(part_tflops, 1),
