@@ -207,3 +207,31 @@ def test_debug_validate_errors(lib):
     import torch
     if torch.cuda.device_count() == 0:
         assert lib.verify_attn_debug_validate(ctypes.byref(p), *args, None) == header_enum("VERIFY_ATTN_ERR_DEVICE")
+
+
+def test_plan_covers_every_split():
+    """For random shapes and random valid sequence lengths (each in
+    [tree_size, max_seq_len], summing to total_kv), the plan's max_splits and
+    grid cover every (split, row tile) item the kernels derive on the device,
+    and the combine's grid covers every output row."""
+    import numpy as np
+    rng = np.random.default_rng(7)
+    for _ in range(400):
+        B = int(rng.integers(1, 140))
+        H = int(rng.choice([1, 2, 8, 16, 64]))
+        T = int(rng.integers(1, 65))
+        lens = rng.integers(T, T + int(rng.choice([1, 50, 3000, 70000])), size=B)
+        max_len = int(lens.max()) + int(rng.choice([0, 0, 1, 999]))
+        total = int(lens.sum())
+        nsplit = int(rng.choice([0, 0, 0, 1, 3, 64]))
+        p = mtv.make_params(num_seqs=B, num_heads=H, tree_size=T, max_seq_len=max_len, total_kv=total,
+                            pool_slots=total + 5, sm_scale=0.07, nsplit=nsplit)
+        plan = mtv.verify_attn_plan(p)
+        c = plan["keys_per_split"]
+        assert c % 32 == 0 and c > 0
+        splits = int(sum(-(-int(n) // c) for n in lens))
+        assert splits <= plan["max_splits"], (B, H, T, max_len, total, nsplit, plan)
+        assert plan["partial_blocks"] >= plan["max_splits"] * plan["row_tiles"]
+        assert plan["row_tiles"] * plan["rows_per_tile"] >= H * T
+        assert mtv.verify_attn_workspace_size(p) == plan["max_splits"] * H * T * (512 + 2) * 4
+        assert mtv.verify_attn_f32_workspace_size(p) > 0
