@@ -12,7 +12,9 @@ total KV bytes exceed twice the 256 MB Infinity Cache, so repeats are served
 from HBM; the K timed steps are recorded in one HIP graph and replayed once,
 bracketed by synchronisation, and timed with HIP events on the launch stream.
 The partial kernel is also timed on its own the same way: that duration gives
-the roofline figure.
+the roofline figure. A library bf16 GEMM is timed in the same run on operands
+drawn like the workload's and on zeros (`mfma_reference`): the matrix cores
+sustain a lower rate on toggling data than the published peak.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Prints one JSON line.
@@ -182,6 +184,39 @@ def measure(name, steps, warmup, nsplit=0, stages=("full", "partial")):
     return res
 
 
+def gemm_reference(n=8192, reps=20):
+    """Sustained bf16 matrix rate of the library GEMM (torch.matmul, n x n x n, fp32
+    accumulate) on operands drawn like the workload's (one factor N(0,1), the other
+    N(0,1)*0.1) and on all-zero operands. The matrix cores draw more power on toggling
+    data, so the rate they sustain depends on the values; this is the reference for how
+    far the partial kernel is from what the chip sustains on such data."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(7)
+    res = {"kind": f"torch.matmul bf16 {n}x{n}x{n}, fp32 accumulate", "reps": reps}
+    for label in ("normal", "zeros"):
+        if label == "normal":
+            a = torch.randn((n, n), generator=g, device="cuda", dtype=torch.float32).mul_(0.1).to(torch.bfloat16)
+            b = torch.randn((n, n), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        else:
+            a = torch.zeros((n, n), device="cuda", dtype=torch.bfloat16)
+            b = torch.zeros((n, n), device="cuda", dtype=torch.bfloat16)
+        c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(reps):
+            torch.matmul(a, b, out=c)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / reps
+        res[f"tflops_{label}_operands"] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+        del a, b, c
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(name, repeats=3):
     """The oracle (fp64 C, OpenMP) on whole calls of the same workload."""
     import oracle
@@ -293,6 +328,8 @@ def main():
                     help="comma-separated extra workloads reported beside the headline ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-f32", action="store_true", help="skip the fp32-input variant line")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the library bf16 GEMM timed as the sustained-matrix-rate reference")
     ap.add_argument("--stage", default=None, choices=[None, "full", "partial", "combine", "append", "compact", "copy"],
                     help="profiling aid: only run K calls of one stage of the headline workload; "
                          "'copy' runs K device-to-device copies of 1 GiB (counter calibration)")
@@ -436,6 +473,10 @@ def main():
             "gbs": round(2 * KV_ROW_BYTES * head["wl"].total_kv / (head["compact_ms"] * 1e-3) / 1e9, 1),
         },
     }
+    if not args.no_gemm_reference:
+        ref = gemm_reference()
+        ref["partial_kernel_frac_of_normal"] = round(part_tflops / ref["tflops_normal_operands"], 4)
+        line["mfma_reference"] = ref
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args.workload)
         line["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)
