@@ -473,6 +473,14 @@ def main():
             "gbs": round(2 * KV_ROW_BYTES * head["wl"].total_kv / (head["compact_ms"] * 1e-3) / 1e9, 1),
         },
     }
+    # the pages' own figures, on their hardware: orientation only, never a target
+    line["pages_context"] = {
+        "hardware": "RTX PRO 6000 Blackwell (sm_120), 1.8 TB/s HBM peak",
+        "triton_verify_effective_gbs": 14,
+        "own_flash_kernel_vs_naive": "1.7-4.2x (all 64 heads, up to 65k context)",
+        "vectorized_bf16_gather": "1.3-1.8x",
+        "end_to_end_decode_vs_triton_graph": "3.0x @4k, 4.3x @16k, 6.1x @65k (8 GPUs, whole model)",
+    }
     if not args.no_gemm_reference:
         ref = gemm_reference()
         ref["partial_kernel_frac_of_normal"] = round(part_tflops / ref["tflops_normal_operands"], 4)
