@@ -88,6 +88,32 @@ def tiny(B=1, H=2, T=4, prefixes=(5,), pool=None, seed=1, tree="random", **kw):
                                 seed=seed, tree=tree, **kw)
 
 
+def numpy_bruteforce(wl) -> np.ndarray:
+    """Dense fp64 brute force in NumPy, independent of the oracle and of torch:
+    per sequence, gather K [N, 576] through the slot list, build the mask matrix
+    M [T, N] (stride N = prefix + T: every prefix column, then the ancestor-or-self
+    closure of the tree), and compute softmax(Q K^T * scale + log M) V with
+    V = K[:, :512]; log 0 = -inf removes the masked keys."""
+    out = np.empty((wl.B, wl.T, wl.H, DV), dtype=np.float64)
+    seg = 0
+    for b in range(wl.B):
+        N = int(wl.seq_lens[b])
+        P = N - wl.T
+        K = _f64(wl.kv_pool[wl.slot_idx[seg:seg + N]])
+        M = np.zeros((wl.T, N), dtype=bool)
+        M[:, :P] = True
+        M[:, P:] = ancestor_closure(wl.tree_parent[b])
+        with np.errstate(divide="ignore"):
+            log_m = np.log(M.astype(np.float64))                      # 0 or -inf
+        S = np.einsum("thd,nd->thn", _f64(wl.q[b]), K) * wl.sm_scale + log_m[:, None, :]
+        S -= S.max(axis=2, keepdims=True)
+        W = np.exp(S)
+        W /= W.sum(axis=2, keepdims=True)
+        out[b] = np.einsum("thn,nv->thv", W, K[:, :DV])
+        seg += N
+    return out
+
+
 def run(orc, wl):
     return orc.run(wl)
 
@@ -356,9 +382,35 @@ def pin_f32_on_bf16_values(orc):
     assert np.array_equal(run(orc, wl), run(orc, wl32))
 
 
+def pin_bruteforce_grid(orc):
+    """Oracle == NumPy dense brute force with an explicit log-mask, over every
+    combination of prefix P in {0, 1, 5, 17, 64}, tree size T in {1, 2, 3, 8, 64}
+    and heads H in {1, 2, 8} (random trees, two seeds each, the second as one
+    sequence of a two-sequence batch), and on the 1,024-slot, 256-token, H=8, T=8
+    configuration itself."""
+    n = 0
+    for P in (0, 1, 5, 17, 64):
+        for T in (1, 2, 3, 8, 64):
+            for H in (1, 2, 8):
+                for rep in range(2):
+                    seed = 500 + 100 * rep + 10 * P + 3 * T + H
+                    if rep == 0:
+                        wl = tiny(B=1, H=H, T=T, prefixes=[P], seed=seed)
+                    else:
+                        wl = tiny(B=2, H=H, T=T, prefixes=[P, (P * 7 + 3) % 19], seed=seed)
+                    err = np.abs(run(orc, wl) - numpy_bruteforce(wl)).max()
+                    assert err <= 1e-12, f"P={P} T={T} H={H} rep={rep}: max |oracle - brute force| = {err}"
+                    n += 1
+    wl = inputs.config("c1_tiny")
+    err = np.abs(run(orc, wl) - numpy_bruteforce(wl)).max()
+    assert err <= 1e-12, f"c1_tiny: max |oracle - brute force| = {err}"
+    assert n == 150
+
+
 ALL_PINS = [
     pin_library_attention, pin_flat_tree_is_decode, pin_chain_tree_is_causal,
     pin_zero_query_is_mean, pin_single_key, pin_weights, pin_slot_permutation,
     pin_tree_relabel, pin_head_subset, pin_sequences_independent, pin_constant_column,
     pin_scale_linear, pin_worked_example, pin_f32_library_attention, pin_f32_on_bf16_values,
+    pin_bruteforce_grid,
 ]
