@@ -85,6 +85,11 @@ def test_e2_production_shape_sampled(orc):
     check_sampled(orc, inputs.config("e2_h8_t9_65k"), n_per_seq=32)
 
 
+def test_e1_full_head_65k_sampled(orc):
+    # the H=64 point at 65k context that bench.py times beside the headline
+    check_sampled(orc, inputs.config("e1_h64_65k"), n_per_seq=32)
+
+
 # ------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("case", [
@@ -141,6 +146,47 @@ def test_length_bound_above_actual(orc, extra):
 @pytest.mark.parametrize("tree", ["flat", "chain"])
 def test_tree_shapes(orc, tree):
     check_full(orc, small(H=4, T=64, prefixes=[300], tree=tree, seed=5))
+
+
+def _relabel_trees(wl):
+    """Renumber every sequence's tree nodes in another topological order (always
+    take the highest-numbered node whose parent is already numbered), moving the
+    query rows and the tree slots with them. Returns the new workload and, per
+    sequence, the map old label -> new label."""
+    import copy
+    new = copy.deepcopy(wl)
+    sigmas = []
+    seg = 0
+    for b in range(wl.B):
+        parent = wl.tree_parent[b]
+        order, done = [], set()
+        while len(order) < wl.T:
+            ready = [u for u in range(wl.T) if u not in done and (parent[u] < 0 or parent[u] in done)]
+            order.append(max(ready))
+            done.add(order[-1])
+        sigma = np.empty(wl.T, dtype=np.int64)
+        sigma[order] = np.arange(wl.T)
+        for u in range(wl.T):
+            new.tree_parent[b, sigma[u]] = -1 if parent[u] < 0 else sigma[parent[u]]
+        N = int(wl.seq_lens[b])
+        base = seg + N - wl.T
+        new.slot_idx[base + sigma] = wl.slot_idx[base:base + wl.T]
+        new.q[b, sigma] = wl.q[b]
+        sigmas.append(sigma)
+        seg += N
+    return new, sigmas
+
+
+def test_tree_relabel_permutes_outputs(orc):
+    # trees deep enough to cross the 32-key tile boundary, two sequences
+    wl = small(B=2, H=8, T=40, prefixes=[1000, 77], seed=29)
+    got = check_full(orc, wl)[0]
+    wl2, sigmas = _relabel_trees(wl)
+    assert not np.array_equal(wl2.tree_parent, wl.tree_parent)
+    got2 = check_full(orc, wl2)[0]
+    for b, sigma in enumerate(sigmas):
+        ok, worst, idx = parity_gate(got2[b, sigma], got[b])
+        assert ok, f"sequence {b}: relabelled row {idx} differs by {worst:.2f} bf16 ulp"
 
 
 def test_single_key_exact():
