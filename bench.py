@@ -349,7 +349,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the verify path has no multi-GPU mode "
-              "(heads, sequences or KV positions would shard across GPUs; see DESIGN.md).",
+              "(heads, sequences or KV positions would shard across GPUs, with one exchange of the "
+              "split partials before the combine for sharded KV positions).",
               file=sys.stderr)
         sys.exit(2)
 
