@@ -1312,23 +1312,33 @@ int make_plan(const verify_attn_params* p, Plan* pl, int rows_per_tile = ROWS_PE
   if (p->nsplit > 0) {
     chunk = ceil_div64(p->max_seq_len, p->nsplit);
   } else {
-    // Try 1, 2, 4, 8 and 16 workgroups per CU and keep the split length with the
-    // lowest estimated time, in units of one tile of nk keys: every round of one
-    // workgroup per CU costs its tiles plus a fixed start and end (about four
-    // tiles: first loads, partial store), and every (split, row tile) item
-    // about a twentieth of a tile of partial traffic (written, then read by
-    // the combine). More, shorter splits fill the last round better but add
-    // fixed costs and partials.
+    // For R = 1, 2, ... rounds of one workgroup per CU, take the shortest split
+    // (a multiple of nk, at least MIN_CHUNK) whose item count fits R rounds
+    // whatever the lengths are: with total_kv keys over num_seqs sequences there
+    // are at most ceil(total_kv / c) + num_seqs - 1 splits. Keep the split with
+    // the lowest estimated time, in units of one tile of nk keys: every round
+    // costs its tiles plus a fixed start and end (about four tiles: first loads,
+    // partial store), and every (split, row tile) item about a twentieth of a
+    // tile of partial traffic (written, then read by the combine). More, shorter
+    // splits fill the last round better but add fixed costs and partials.
+    const int64_t split_cap = ceil_div64(p->max_seq_len, nk) * nk;  // one split per sequence
+    const int64_t floor_c = ceil_div64(MIN_CHUNK, nk) * nk;
+    // fewest rounds with room for every sequence's last split
+    const int64_t r0 = ceil_div64((int64_t)p->num_seqs * row_tiles, NUM_CUS);
     int64_t best = 0, best_cost = INT64_MAX;
-    for (int64_t per_cu = 1; per_cu <= 16; per_cu *= 2) {
-      int64_t c = ceil_div64(p->total_kv * row_tiles, NUM_CUS * per_cu);
+    for (int64_t R = r0 < 1 ? 1 : r0; R < r0 + 64; ++R) {
+      const int64_t splits = NUM_CUS * R / row_tiles - (p->num_seqs - 1);
+      if (splits < 1) continue;
+      int64_t c = ceil_div64(p->total_kv, splits);
       c = ceil_div64(c < MIN_CHUNK ? MIN_CHUNK : c, nk) * nk;
+      if (c > split_cap) c = split_cap;
       const int64_t items = (ceil_div64(p->total_kv, c) + p->num_seqs - 1) * row_tiles;
       const int64_t cost = ceil_div64(items, NUM_CUS) * (20 * (c / nk) + 20 * ROUND_COST_TILES) + items;
       if (cost < best_cost) {
         best_cost = cost;
         best = c;
       }
+      if (c <= floor_c) break;  // more rounds cannot shorten the split further
     }
     chunk = best;
   }
