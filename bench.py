@@ -187,20 +187,22 @@ def measure(name, steps, warmup, nsplit=0, stages=("full", "partial")):
 def gemm_reference(n=8192, reps=20):
     """Sustained bf16 matrix rate of the library GEMM (torch.matmul, n x n x n, fp32
     accumulate) on operands drawn like the workload's (one factor N(0,1), the other
-    N(0,1)*0.1) and on all-zero operands. The matrix cores draw more power on toggling
+    N(0,1)*0.1) and on all-zero operands, and the fp32 GEMM's rate on the former. The matrix cores draw more power on toggling
     data, so the rate they sustain depends on the values; this is the reference for how
     far the partial kernel is from what the chip sustains on such data."""
     import torch
+    torch.backends.cuda.matmul.allow_tf32 = False  # the fp32 GEMM stays in binary32
     g = torch.Generator(device="cuda").manual_seed(7)
-    res = {"kind": f"torch.matmul bf16 {n}x{n}x{n}, fp32 accumulate", "reps": reps}
-    for label in ("normal", "zeros"):
-        if label == "normal":
-            a = torch.randn((n, n), generator=g, device="cuda", dtype=torch.float32).mul_(0.1).to(torch.bfloat16)
-            b = torch.randn((n, n), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    res = {"kind": f"torch.matmul bf16 {n}x{n}x{n}, fp32 accumulate (and the same in fp32)", "reps": reps}
+    for label in ("normal", "zeros", "f32_normal"):
+        dt = torch.float32 if label == "f32_normal" else torch.bfloat16
+        if label == "zeros":
+            a = torch.zeros((n, n), device="cuda", dtype=dt)
+            b = torch.zeros((n, n), device="cuda", dtype=dt)
         else:
-            a = torch.zeros((n, n), device="cuda", dtype=torch.bfloat16)
-            b = torch.zeros((n, n), device="cuda", dtype=torch.bfloat16)
-        c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+            a = torch.randn((n, n), generator=g, device="cuda", dtype=torch.float32).mul_(0.1).to(dt)
+            b = torch.randn((n, n), generator=g, device="cuda", dtype=torch.float32).to(dt)
+        c = torch.empty((n, n), device="cuda", dtype=dt)
         for _ in range(3):
             torch.matmul(a, b, out=c)
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -485,6 +487,8 @@ def main():
     if not args.no_gemm_reference:
         ref = gemm_reference()
         ref["partial_kernel_frac_of_normal"] = round(part_tflops / ref["tflops_normal_operands"], 4)
+        if f32 is not None:
+            f32["mfma_f32_frac_of_library_f32"] = round(f32["mfma_f32_tflops"] / ref["tflops_f32_normal_operands"], 4)
         line["mfma_reference"] = ref
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args.workload)
