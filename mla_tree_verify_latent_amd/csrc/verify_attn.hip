@@ -797,13 +797,18 @@ void verify_attn_partial_kernel(PartialArgs a) {
 //     lane (m = l%16, g) gives K[m, f] (one 16-byte LDS read per chunk c
 //     serves 4 steps) and Q[n = l%16, f] (held in 144 VGPRs); lane l then
 //     holds S for row l%16, keys 4 g + i.
-//   O^T[e, n] += V[k, e] P[n, k]    k = 4 g + i, step i, 16-feature block e0:
-//     B = P is the lane's own weight for key 4 g + i (no exchange), A = V
-//     from one 4-byte LDS read per lane. O (128 fp32 per lane: row l%16,
-//     features 16 e0 + 4 g + i) stays in AGPRs.
+//   O^T[e, n] += V[k, e] P[n, k]    k = 4 g + i, step i, 16-feature block e:
+//     B = P is the lane's own weight for key 4 g + i (no exchange). Block e
+//     holds the features 64 (e / 4) + 4 m + e % 4 (m = 0..15), so that one
+//     16-byte LDS read of lane (m, g) - features 64 J + 4 m .. +3 of key row
+//     4 g + i - gives the A operands of blocks 4 J .. 4 J + 3. O (128 fp32 per
+//     lane) stays in AGPRs; lane (n, g) holds, in register j of block e, the
+//     feature 64 (e / 4) + 16 g + 4 j + e % 4 of row n, so the four blocks of
+//     a group store one contiguous 16-byte piece per register.
 // The XOR layout keeps both read patterns free of bank conflicts: the 16-byte
 // K reads of 8 consecutive rows land on 8 distinct positions of a 128-byte
-// window, and the 4-byte V reads of keys 4g + i (g = 0..3) on distinct banks.
+// window, and the 16 lanes of a V read that share a key row read 16 distinct
+// positions of one 256-byte window.
 constexpr int F_NK = 16;                          // keys per tile
 constexpr int F_ROWS_PER_WAVE = 16;               // query rows per wave (MFMA N)
 constexpr int F_ROWS_PER_TILE = NWAVES * F_ROWS_PER_WAVE;  // 64
@@ -955,18 +960,12 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
 #pragma unroll
   for (int c3 = 0; c3 < 4; ++c3)
     k_off[c3] = l16 * F_ROW_BYTES + ((((c3 ^ (l16 >> 2)) << 2) | (grp ^ (l16 & 3))) << 4);
-  // V read (key step i, feature block e): lane (feature 16 e + l16, group grp)
-  // reads float l16 % 4 of piece 4 e + l16 / 4 of key row r = 4 grp + i, at
-  // position (4 e + l16 / 4) ^ r = 16 (e / 4) + 4 ((e % 4) ^ grp) + ((l16 / 4) ^ i):
-  // a per-lane base for each (i, e % 4) plus 256 (e / 4).
-  uint32_t v_off[4][4];
+  // V read (key step i, block group J): lane (m = l16, group grp) reads piece
+  // 16 J + l16 of key row r = 4 grp + i (features 64 J + 4 l16 .. +3), stored at
+  // position 16 J + (l16 ^ r % 16): a per-lane base for each i plus 256 J.
+  uint32_t v_off[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e3 = 0; e3 < 4; ++e3)
-      v_off[i][e3] = (4 * grp + i) * F_ROW_BYTES + ((((e3 ^ grp) << 2) | ((l16 >> 2) ^ i)) << 4) + 4 * (l16 & 3);
-  // V read (block e0, step i): lane (feature 16 e0 + l16, group grp) reads
-  // float l16 % 4 of piece 4 e0 + l16 / 4 of key row 4 grp + i.
+  for (int i = 0; i < 4; ++i) v_off[i] = (4 * grp + i) * F_ROW_BYTES + ((l16 ^ ((4 * grp + i) & 15)) << 4);
   f32x4 o[F_PV_BLOCKS];
 #pragma unroll
   for (int e = 0; e < F_PV_BLOCKS; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -982,13 +981,13 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
     const bool more = it + 2 < ntiles;
 #pragma unroll
     for (int lr = 0; lr < 4; ++lr) sn[lr] = band_slot(more ? kt + 2 * F_NK : kt, lr);
-    // ---- S^T = K Q^T: 36 chunks x 4 MFMAs, two accumulators (even / odd chunks)
+    // ---- S^T = K Q^T: 36 chunks x 4 MFMAs, two accumulators (even / odd k-steps)
     f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     uint32_t kb[4];  // per-tile bases; chunk c reads kb[c % 4] + 256 (c / 4)
 #pragma unroll
     for (int c3 = 0; c3 < 4; ++c3) kb[c3] = cur + k_off[c3];
     auto kread = [&](int c) { return *(const LDS_AS f32x4*)(uintptr_t)(kb[c & 3] + 256 * (c >> 2)); };
-    constexpr int FK_AHEAD = 6;  // K reads in flight
+    constexpr int FK_AHEAD = 4;  // K reads in flight
     f32x4 kbuf[FK_AHEAD];
 #pragma unroll
     for (int c = 0; c < FK_AHEAD; ++c) kbuf[c] = kread(c);
@@ -998,7 +997,7 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
       if (c + FK_AHEAD < F_CHUNKS) kbuf[c % FK_AHEAD] = kread(c + FK_AHEAD);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        sacc[c & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[i], qf[c][i], sacc[c & 1], 0, 0, 0);
+        sacc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[i], qf[c][i], sacc[i & 1], 0, 0, 0);
       if (c == F_CHUNKS / 2 && more) gather(it + 2, sn);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1030,27 +1029,26 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
       for (int e = 0; e < F_PV_BLOCKS; ++e) acc_scale4(o[e], alpha);
       mfma_valu_gap();
     }
-    // ---- O^T += V^T P^T: 4 key steps x 32 feature blocks (consecutive MFMAs
-    // use different accumulators)
+    // ---- O^T += V^T P^T: 4 key steps x 8 block groups x 4 blocks, one 16-byte
+    // V read per group (consecutive MFMAs use different accumulators)
     mfma_valu_gap();
-    uint32_t vb[4][4];
+    uint32_t vb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e3 = 0; e3 < 4; ++e3) vb[i][e3] = cur + v_off[i][e3];
-    auto vread = [&](int st) {  // step st = 32 i + e
-      const int i = st >> 5, e = st & 31;
-      return *(const LDS_AS float*)(uintptr_t)(vb[i][e & 3] + 256 * (e >> 2));
+    for (int i = 0; i < 4; ++i) vb[i] = cur + v_off[i];
+    auto vread = [&](int st) {  // step st = 8 i + J
+      return *(const LDS_AS f32x4*)(uintptr_t)(vb[st >> 3] + 256 * (st & 7));
     };
-    constexpr int V_AHEAD = 16;
-    float vbuf[V_AHEAD];
+    constexpr int V_AHEAD = 4;  // V reads in flight
+    f32x4 vbuf[V_AHEAD];
 #pragma unroll
     for (int st = 0; st < V_AHEAD; ++st) vbuf[st] = vread(st);
 #pragma unroll
-    for (int st = 0; st < 4 * F_PV_BLOCKS; ++st) {
-      const float v = vbuf[st % V_AHEAD];
-      if (st + V_AHEAD < 4 * F_PV_BLOCKS) vbuf[st % V_AHEAD] = vread(st + V_AHEAD);
-      mfma16_acc(o[st & 31], v, pw[st >> 5]);
+    for (int st = 0; st < F_PV_BLOCKS; ++st) {
+      const f32x4 v = vbuf[st % V_AHEAD];
+      if (st + V_AHEAD < F_PV_BLOCKS) vbuf[st % V_AHEAD] = vread(st + V_AHEAD);
+      const int J = st & 7;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) mfma16_acc(o[4 * J + e4], v[e4], pw[st >> 3]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -1065,7 +1063,11 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
     const int64_t rowid = (int64_t)g * a.M + qrow;
     float* po = a.part_o + rowid * V_DIM + 4 * grp;
 #pragma unroll
-    for (int e = 0; e < F_PV_BLOCKS; ++e) *reinterpret_cast<f32x4*>(po + 16 * e) = o[e];
+    for (int J = 0; J < F_PV_BLOCKS / 4; ++J)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)  // feature 64 J + 16 grp + 4 j
+        *reinterpret_cast<f32x4*>(po + 64 * J + 12 * grp + 4 * j) =
+            f32x4{o[4 * J][j], o[4 * J + 1][j], o[4 * J + 2][j], o[4 * J + 3][j]};
     if (grp == 0) {
       a.part_ml[2 * rowid] = m_run;
       a.part_ml[2 * rowid + 1] = l_row;
