@@ -890,24 +890,33 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
     g_row[j] = lr;
     g_piece[j] = ((o - lr * F_ROW_BYTES) >> 4) ^ (r & 15);
   }
-  // Slot of row lr (0..3) of this wave's band of the tile at key kt; keys past
-  // the split end repeat its last key.
-  auto band_slot = [&](int kt, int lr) {
-    int key = kt + wave * (F_NK / NWAVES) + lr;
+  // Slot-table entries of this wave's 4-row band of the tile at key kt, as one
+  // vector load: lane l reads the entry of row l % 4 (keys past the split end
+  // repeat its last key). band_slots() clamps them and reads them out to
+  // wave-uniform values where the gather needs them, a tile after the load, so
+  // that its round trip overlaps the work in between (four scalar loads, each
+  // waited for before the next, would stall the wave four round trips).
+  auto band_load = [&](int kt) {
+    int key = kt + wave * (F_NK / NWAVES) + (lane & 3);
     key = key < k1 ? key : k1 - 1;
     int64_t si = loc.seg + key;
     si = si < slot_hi ? si : slot_hi;
-    int slot = a.slot_idx[si];
-    return slot < 0 ? 0 : (slot > pool_hi ? pool_hi : slot);
+    return a.slot_idx[si];
+  };
+  auto band_slots = [&](int v, int (&out)[4]) {
+    const int slot = v < 0 ? 0 : (v > pool_hi ? pool_hi : v);
+#pragma unroll
+    for (int lr = 0; lr < 4; ++lr) out[lr] = __builtin_amdgcn_readlane(slot, lr);
+  };
+  auto gather_one = [&](int t, const int (&slots)[4], int j) {  // load j of tile t
+    const uint32_t dst = smem_base + (t % F_NBUF) * F_TILE_BYTES + wave * (F_NK / NWAVES) * F_ROW_BYTES;
+    const int lr = g_row[j];
+    const int slot = lr == 0 ? slots[0] : (lr == 1 ? slots[1] : (lr == 2 ? slots[2] : slots[3]));
+    load_to_lds16(a.kv + (int64_t)slot * KV_DIM + 4 * g_piece[j], dst + j * 1024);
   };
   auto gather = [&](int t, const int (&slots)[4]) {
-    const uint32_t dst = smem_base + (t % F_NBUF) * F_TILE_BYTES + wave * (F_NK / NWAVES) * F_ROW_BYTES;
 #pragma unroll
-    for (int j = 0; j < F_LOADS; ++j) {
-      const int lr = g_row[j];
-      const int slot = lr == 0 ? slots[0] : (lr == 1 ? slots[1] : (lr == 2 ? slots[2] : slots[3]));
-      load_to_lds16(a.kv + (int64_t)slot * KV_DIM + 4 * g_piece[j], dst + j * 1024);
-    }
+    for (int j = 0; j < F_LOADS; ++j) gather_one(t, slots, j);
   };
 
   // Prologue: parent pointers, the slots and gathers of tiles 0 and 1, the
@@ -915,12 +924,10 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
   int parent = -1;
   if (wave == 0 && lane < a.T) parent = a.tree_parent[(int64_t)loc.b * a.T + lane];
   {
+    const int v0 = band_load(k0), v1 = band_load(k0 + F_NK);
     int s0[4], s1[4];
-#pragma unroll
-    for (int lr = 0; lr < 4; ++lr) {
-      s0[lr] = band_slot(k0, lr);
-      s1[lr] = band_slot(k0 + F_NK, lr);
-    }
+    band_slots(v0, s0);
+    band_slots(v1, s1);
     gather(0, s0);
     gather(1, s1);
   }
@@ -971,16 +978,19 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
   for (int e = 0; e < F_PV_BLOCKS; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
+  int slot_pre = band_load(2 < ntiles ? k0 + 2 * F_NK : k0);  // slot entries of tile 2
   for (int it = 0; it < ntiles; ++it) {
     wait_vmcnt<0>();  // own share of tile it (and of it+1) landed
     lds_barrier();    // tile it complete; every wave is done with tile it-1
     const uint32_t cur = smem_base + (it % F_NBUF) * F_TILE_BYTES;
     const int kt = k0 + it * F_NK;
-    // slots of tile it+2 (their gather goes out halfway through this QK)
-    int sn[4];
+    // The gather of tile it+2 rides on this QK, one load every two chunks (a
+    // burst of nine loads stalls the wave for most of their issue); its slot
+    // entries were loaded during tile it-1, and those of tile it+3 go out now.
     const bool more = it + 2 < ntiles;
-#pragma unroll
-    for (int lr = 0; lr < 4; ++lr) sn[lr] = band_slot(more ? kt + 2 * F_NK : kt, lr);
+    const int slot_next = slot_pre;
+    slot_pre = band_load(it + 3 < ntiles ? kt + 3 * F_NK : kt);
+    int sn[4] = {0, 0, 0, 0};
     // ---- S^T = K Q^T: 36 chunks x 4 MFMAs, two accumulators (even / odd k-steps)
     f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     uint32_t kb[4];  // per-tile bases; chunk c reads kb[c % 4] + 256 (c / 4)
@@ -998,7 +1008,8 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         sacc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[i], qf[c][i], sacc[i & 1], 0, 0, 0);
-      if (c == F_CHUNKS / 2 && more) gather(it + 2, sn);
+      if (more && c == 1) band_slots(slot_next, sn);
+      if (more && c >= 2 && (c - 2) % 2 == 0 && (c - 2) / 2 < F_LOADS) gather_one(it + 2, sn, (c - 2) / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
     // ---- scale, mask, online softmax (base 2); lane: row l16, keys 4 grp + i
@@ -1038,7 +1049,7 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
     auto vread = [&](int st) {  // step st = 8 i + J
       return *(const LDS_AS f32x4*)(uintptr_t)(vb[st >> 3] + 256 * (st & 7));
     };
-    constexpr int V_AHEAD = 4;  // V reads in flight
+    constexpr int V_AHEAD = 3;  // V reads in flight (more spill registers)
     f32x4 vbuf[V_AHEAD];
 #pragma unroll
     for (int st = 0; st < V_AHEAD; ++st) vbuf[st] = vread(st);
