@@ -363,6 +363,13 @@ __device__ __forceinline__ float xor32(float x) {
   return __builtin_bit_cast(float, ((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
 }
 
+// Value of lane l ^ 16 (gfx950 permlane swap of 16-lane rows; plain VALU).
+__device__ __forceinline__ float xor16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, ((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   u += 0x7fffu + ((u >> 16) & 1u);
@@ -1023,8 +1030,8 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
       sv[i] = vis ? (sacc[0][i] + sacc[1][i]) * a.qk_scale_log2 : -INFINITY;
     }
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, xor16(mx));  // the four lane groups hold keys of the same row
+    mx = fmaxf(mx, xor32(mx));
     const bool raise = mx > m_run + LAZY_RESCALE_LOG2;
     const bool rescale = __ballot(raise & (m_run != -INFINITY)) != 0;  // rows with weights so far
     const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
