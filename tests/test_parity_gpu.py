@@ -100,6 +100,7 @@ def test_e1_full_head_65k_sampled(orc):
     dict(B=1, H=64, T=3, prefixes=[1000]),             # 192 rows, 3 row tiles
     dict(B=1, H=16, T=9, prefixes=[4097]),             # tail tile of 1 key + tree
     dict(B=4, H=8, T=16, prefixes=[5000, 1, 32, 2047]),
+    dict(B=1, H=128, T=64, prefixes=[2000]),           # 8,192 rows: 64 row tiles, T at its maximum
 ], ids=lambda c: "B{B}_H{H}_T{T}_P{prefixes}".format(**c))
 def test_edge_shapes(orc, case):
     check_full(orc, small(**case))
