@@ -1378,7 +1378,8 @@ int make_plan(const verify_attn_params* p, Plan* pl, int rows_per_tile = ROWS_PE
   // CUs read the partials.
   const int halves = (wpr == 16 && rows * 16 * 2 <= COMBINE_WAVES) ? 2 : 1;
   const int64_t cblocks = ceil_div64(rows, (wpr < 4 ? 4 : wpr) / wpr) * halves;
-  if (blocks > INT32_MAX || cblocks > INT32_MAX || max_splits > INT32_MAX) return VERIFY_ATTN_ERR_BAD_DIM;
+  if (blocks > INT32_MAX || cblocks > INT32_MAX || max_splits > INT32_MAX || chunk > INT32_MAX)
+    return VERIFY_ATTN_ERR_BAD_DIM;
   pl->M = (int)M;
   pl->row_tiles = (int)row_tiles;
   pl->chunk = (int)chunk;

@@ -235,3 +235,12 @@ def test_plan_covers_every_split():
         assert plan["row_tiles"] * plan["rows_per_tile"] >= H * T
         assert mtv.verify_attn_workspace_size(p) == plan["max_splits"] * H * T * (512 + 2) * 4
         assert mtv.verify_attn_f32_workspace_size(p) > 0
+
+
+def test_split_length_overflow_rejected():
+    """A split length that rounds past INT32_MAX (one split of a 2^31 - 1 token bound) is
+    refused as invalid params instead of wrapping."""
+    p = base_params(max_seq_len=2**31 - 1, total_kv=2**31 - 1, nsplit=1)
+    assert mtv.verify_attn_workspace_size(p) == 0
+    ok = base_params(max_seq_len=2**31 - 64, total_kv=2**31 - 64, nsplit=1)
+    assert mtv.verify_attn_workspace_size(ok) > 0
