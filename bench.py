@@ -219,7 +219,7 @@ def gemm_reference(n=8192, reps=20):
     return res
 
 
-def cpu_baseline(name, repeats=3):
+def cpu_baseline(name, repeats=5):
     """The oracle (fp64 C, OpenMP) on whole calls of the same workload."""
     import oracle
     from synthetic import inputs
@@ -243,7 +243,7 @@ def cpu_baseline(name, repeats=3):
         "value": algorithmic_bytes(wl) / t / 1e9, "unit": "GB/s", "cores": orc.num_threads(),
         "kind": "oracle", "cpu_model": model, "nproc": os.cpu_count(),
         "sample": f"{name}: whole call ({wl.B * wl.T * wl.H} output rows), median of {repeats} "
-                  f"calls, {t:.2f} s per call",
+                  f"calls, {t:.2f} s per call ({sum(times):.1f} s of oracle time in all)",
         "s_per_call": t,
     }
 
