@@ -9,7 +9,9 @@ output rows); this module compiles it with gcc and calls it through ctypes.
 
 Parity status of each oracle function (pins live in tests/test_oracle_pins.py):
   oracle_verify_attn / oracle_verify_attn_rows: pinned (library attention with
-      an explicit mask, closed forms, invariants, planted-mistake checks).
+      an explicit mask, a NumPy dense brute force with a log-mask over 150
+      random small shapes and the tiny configuration, closed forms, invariants,
+      planted-mistake checks).
   oracle_verify_attn_f32 / oracle_verify_attn_rows_f32 (binary32 q and KV):
       pinned (library attention with an explicit mask on fp32 data; bit-equal
       to the bf16 entry points when the fp32 values are bf16 values).
