@@ -62,7 +62,8 @@ extern "C" {
 enum verify_attn_status {
   VERIFY_ATTN_OK = 0,
   VERIFY_ATTN_ERR_NULL_PTR = -1,            /* a required pointer is NULL */
-  VERIFY_ATTN_ERR_BAD_DIM = -2,             /* B/H < 1, kv_dim != 576, v_dim != 512, ... */
+  VERIFY_ATTN_ERR_BAD_DIM = -2,             /* B/H < 1, kv_dim != 576, v_dim != 512, H*T > 2^20,
+                                               a grid, split count or split length past 2^31 - 1, ... */
   VERIFY_ATTN_ERR_TREE_TOO_LARGE = -3,      /* tree_size outside 1..64 */
   VERIFY_ATTN_ERR_MISALIGNED = -4,          /* q/kv_pool/out/workspace not 16-byte aligned */
   VERIFY_ATTN_ERR_WORKSPACE_TOO_SMALL = -5, /* workspace_bytes < verify_attn_workspace_size() */
