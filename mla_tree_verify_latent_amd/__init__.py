@@ -72,6 +72,10 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
                           "`python -m mla_tree_verify_latent_amd.build` (hipcc, gfx950)")
+    # torch first: its bundled HIP runtime has the system runtime's soname, so the
+    # library then binds to the runtime that owns torch's tensors and streams (loaded
+    # the other way round, torch would bring a second runtime into the process).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, vp, i32p = ctypes.POINTER(Params), ctypes.c_void_p, ctypes.c_void_p
     lib.verify_attn_workspace_size.argtypes = [P]

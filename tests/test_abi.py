@@ -244,3 +244,18 @@ def test_split_length_overflow_rejected():
     assert mtv.verify_attn_workspace_size(p) == 0
     ok = base_params(max_seq_len=2**31 - 64, total_kv=2**31 - 64, nsplit=1)
     assert mtv.verify_attn_workspace_size(ok) > 0
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Loading the library before torch must not put a second HIP runtime in the
+    process: torch's bundled runtime has the same soname as the system one, and the
+    library has to bind to the copy that torch's tensors and streams belong to."""
+    import subprocess
+    import sys
+    code = ("import mla_tree_verify_latent_amd as m; m.load_library(); import torch; "
+            "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}; "
+            "print(len(paths))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
