@@ -177,6 +177,31 @@ def _check_tensors(q, kv_pool, slot_idx, seq_lens, tree_parent, out=None, dtype=
         raise ValueError("out must be [B, T, H, 512]")
 
 
+def _check_sizes(params: Params, *, q=None, kv_pool=None, slot_idx=None, seq_lens=None,
+                 tree_parent=None, out=None):
+    """The tensors must hold what `params` says they hold: the kernels index them by
+    these sizes, so a tensor smaller than its params would be read or written past
+    its end."""
+    B, T, H = int(params.num_seqs), int(params.tree_size), int(params.num_heads)
+    if q is not None and tuple(q.shape) != (B, T, H, KV_DIM):
+        raise ValueError(f"q is {tuple(q.shape)}, params say [{B}, {T}, {H}, {KV_DIM}]")
+    if out is not None and tuple(out.shape) != (B, T, H, V_DIM):
+        raise ValueError(f"out is {tuple(out.shape)}, params say [{B}, {T}, {H}, {V_DIM}]")
+    if kv_pool is not None and int(kv_pool.shape[0]) < int(params.pool_slots):
+        raise ValueError(f"kv_pool has {kv_pool.shape[0]} rows, params say pool_slots={params.pool_slots}")
+    if slot_idx is not None and slot_idx.numel() != int(params.total_kv):
+        raise ValueError(f"slot_idx has {slot_idx.numel()} entries, params say total_kv={params.total_kv}")
+    if seq_lens is not None and tuple(seq_lens.shape) != (B,):
+        raise ValueError(f"seq_lens is {tuple(seq_lens.shape)}, params say [{B}]")
+    if tree_parent is not None and tuple(tree_parent.shape) != (B, T):
+        raise ValueError(f"tree_parent is {tuple(tree_parent.shape)}, params say [{B}, {T}]")
+
+
+def _check_workspace(workspace):
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+
+
 def params_for(q, kv_pool, slot_idx, *, max_seq_len: int, sm_scale: float, nsplit: int = 0,
                page_size: int = 1) -> Params:
     """Params of a call on these tensors. max_seq_len is host-known by the caller."""
@@ -190,6 +215,9 @@ def verify_attn(q, kv_pool, slot_idx, seq_lens, tree_parent, out, workspace, par
                 stream=None) -> None:
     """Enqueue the verify attention on `stream` (default: torch's current stream)."""
     _check_tensors(q, kv_pool, slot_idx, seq_lens, tree_parent, out)
+    _check_sizes(params, q=q, kv_pool=kv_pool, slot_idx=slot_idx, seq_lens=seq_lens,
+                 tree_parent=tree_parent, out=out)
+    _check_workspace(workspace)
     _check(load_library().verify_attn(
         ctypes.byref(params), _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
         _ptr(tree_parent), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -205,6 +233,9 @@ def verify_attn_f32(q, kv_pool, slot_idx, seq_lens, tree_parent, out, workspace,
     """Enqueue the fp32-input verify attention (float32 q, kv_pool and out)."""
     import torch
     _check_tensors(q, kv_pool, slot_idx, seq_lens, tree_parent, out, dtype=torch.float32)
+    _check_sizes(params, q=q, kv_pool=kv_pool, slot_idx=slot_idx, seq_lens=seq_lens,
+                 tree_parent=tree_parent, out=out)
+    _check_workspace(workspace)
     _check(load_library().verify_attn_f32(
         ctypes.byref(params), _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
         _ptr(tree_parent), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -220,8 +251,14 @@ def verify_attn_debug_validate(slot_idx, seq_lens, tree_parent, params: Params, 
     """Check the device-resident inputs; returns the BAD_* bits (0 = valid).
     Debug only: reads the result back (synchronises the stream)."""
     import torch
+    for name, t in dict(slot_idx=slot_idx, seq_lens=seq_lens, tree_parent=tree_parent).items():
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.int32:
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    _check_sizes(params, slot_idx=slot_idx, seq_lens=seq_lens, tree_parent=tree_parent)
     if flags is None:
         flags = torch.empty(1, dtype=torch.int32, device=slot_idx.device)
+    elif not flags.is_cuda or flags.dtype != torch.int32 or flags.numel() < 1:
+        raise ValueError("flags must be an int32 device tensor of at least one element")
     _check(load_library().verify_attn_debug_validate(
         ctypes.byref(params), _ptr(slot_idx), _ptr(seq_lens), _ptr(tree_parent), _ptr(flags),
         _stream(stream)))
@@ -231,6 +268,9 @@ def verify_attn_debug_validate(slot_idx, seq_lens, tree_parent, params: Params, 
 def verify_attn_partial(q, kv_pool, slot_idx, seq_lens, tree_parent, workspace, params: Params,
                         stream=None) -> None:
     _check_tensors(q, kv_pool, slot_idx, seq_lens, tree_parent)
+    _check_sizes(params, q=q, kv_pool=kv_pool, slot_idx=slot_idx, seq_lens=seq_lens,
+                 tree_parent=tree_parent)
+    _check_workspace(workspace)
     _check(load_library().verify_attn_partial(
         ctypes.byref(params), _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
         _ptr(tree_parent), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -238,6 +278,14 @@ def verify_attn_partial(q, kv_pool, slot_idx, seq_lens, tree_parent, workspace, 
 
 
 def verify_attn_combine(seq_lens, out, workspace, params: Params, stream=None) -> None:
+    import torch
+    for name, t in dict(seq_lens=seq_lens, out=out).items():
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if seq_lens.dtype != torch.int32 or out.dtype != torch.bfloat16:
+        raise ValueError("seq_lens must be int32 and out bfloat16")
+    _check_sizes(params, seq_lens=seq_lens, out=out)
+    _check_workspace(workspace)
     _check(load_library().verify_attn_combine(
         ctypes.byref(params), _ptr(seq_lens), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -258,6 +306,7 @@ def verify_attn_append_kv(kv_new, slot_idx, seq_lens, kv_pool, params: Params, s
         raise ValueError("kv_new must be [B, T, 576]")
     if kv_pool.dim() != 2 or kv_pool.shape[1] != KV_DIM:
         raise ValueError("kv_pool must be [slots, 576]")
+    _check_sizes(params, kv_pool=kv_pool, slot_idx=slot_idx, seq_lens=seq_lens)
     _check(load_library().verify_attn_append_kv(
         ctypes.byref(params), _ptr(kv_new), _ptr(slot_idx), _ptr(seq_lens), _ptr(kv_pool),
         _stream(stream)))
@@ -273,6 +322,7 @@ def verify_attn_compact_kv(kv_pool, slot_idx, kv_dst, params: Params, stream=Non
         raise ValueError("kv_pool / kv_dst must be bfloat16, slot_idx int32")
     if tuple(kv_dst.shape) != (int(params.total_kv), KV_DIM) or kv_pool.dim() != 2 or kv_pool.shape[1] != KV_DIM:
         raise ValueError("kv_dst must be [total_kv, 576] and kv_pool [slots, 576]")
+    _check_sizes(params, kv_pool=kv_pool, slot_idx=slot_idx)
     _check(load_library().verify_attn_compact_kv(
         ctypes.byref(params), _ptr(kv_pool), _ptr(slot_idx), _ptr(kv_dst), _stream(stream)))
 

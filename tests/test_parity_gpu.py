@@ -315,3 +315,38 @@ def test_host_errors_raise_without_launch():
     with pytest.raises(mtv.VerifyAttnError) as e:
         mtv.verify_attn(**dev, out=out, workspace=ws, params=prm)
     assert e.value.status == -5
+
+
+def test_binding_refuses_tensors_smaller_than_params():
+    # the kernels index by the params' sizes: the binding checks the tensors hold them
+    import torch
+    import mla_tree_verify_latent_amd as mtv
+    wl = small(seed=17)
+    dev = to_device(wl)
+    prm = params_of(wl)
+    ws = torch.empty(mtv.verify_attn_workspace_size(prm), dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.B, wl.T, wl.H, 512), dtype=torch.bfloat16, device="cuda")
+    def with_(**kw):
+        p = mtv.make_params(num_seqs=wl.B, num_heads=wl.H, tree_size=wl.T, max_seq_len=wl.max_seq_len,
+                            total_kv=wl.total_kv, pool_slots=wl.pool_slots, sm_scale=wl.sm_scale)
+        for k, v in kw.items():
+            setattr(p, k, v)
+        return p
+    for p in (with_(pool_slots=wl.pool_slots + 1), with_(total_kv=wl.total_kv + 1),
+              with_(num_heads=wl.H * 2), with_(tree_size=wl.T - 1), with_(num_seqs=wl.B + 1)):
+        with pytest.raises(ValueError):
+            mtv.verify_attn(**dev, out=out, workspace=ws, params=p)
+        with pytest.raises(ValueError):
+            mtv.verify_attn_partial(**dev, workspace=ws, params=p)
+    with pytest.raises(ValueError):
+        mtv.verify_attn_combine(dev["seq_lens"], out[:, :-1], ws, prm)
+    with pytest.raises(ValueError):
+        mtv.verify_attn_combine(dev["seq_lens"], out.float(), ws, prm)
+    with pytest.raises(ValueError):
+        mtv.verify_attn_debug_validate(dev["slot_idx"][:-1], dev["seq_lens"], dev["tree_parent"], prm)
+    with pytest.raises(ValueError):
+        mtv.verify_attn_debug_validate(dev["slot_idx"], dev["seq_lens"], dev["tree_parent"], prm,
+                                       flags=torch.zeros(1, dtype=torch.float32, device="cuda"))
+    # the matching call still runs
+    mtv.verify_attn(**dev, out=out, workspace=ws, params=prm)
+    torch.cuda.synchronize()
