@@ -164,7 +164,7 @@ def replicas_for(wl) -> int:
     return max(1, math.ceil(2 * MALL_BYTES / max(1, wl.kv_bytes())))
 
 
-def measure(name, steps, warmup, nsplit=0, stages=("full", "partial")):
+def measure(name, steps, warmup, nsplit=0, stages=("full", "partial"), repeats=3):
     from synthetic import inputs
     wl = inputs.config(name)
     R = replicas_for(wl)
@@ -172,7 +172,7 @@ def measure(name, steps, warmup, nsplit=0, stages=("full", "partial")):
     res = {"workload": name, "replicas": R,
            "plan": None if wl.f32 else b.mtv.verify_attn_plan(b.params)}
     for st in stages:
-        ms, all_ms = b.time_graph(steps, warmup, st)
+        ms, all_ms = b.time_graph(steps, warmup, st, repeats=repeats)
         res[f"{st}_ms"] = ms
         res[f"{st}_ms_repeats"] = all_ms
     warm = Bench(wl, 1, nsplit)
@@ -383,7 +383,8 @@ def main():
         print(json.dumps({"stage": args.stage, "workload": args.workload, "calls": args.warmup + args.steps}))
         return
 
-    head = measure(args.workload, args.steps, args.warmup, stages=("full", "partial", "append", "compact"))
+    head = measure(args.workload, args.steps, args.warmup, stages=("full", "partial", "append", "compact"),
+                   repeats=10)
     ms = head["full_ms"]
     gbs = head["bytes"] / (ms * 1e-3) / 1e9
     part_ms = head["partial_ms"]
@@ -444,6 +445,10 @@ def main():
         "binding_roof_frac": round(max(head["bytes"] / (HBM_PEAK_GBS * 1e9),
                                        head["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3), 4),
         "ms_per_step_repeats": [round(x, 5) for x in head["full_ms_repeats"]],
+        # spread of the per-call time over the 10 timed graph replays of K calls each
+        "ms_per_step_p10_p90": [round(float(np.percentile(head["full_ms_repeats"], q)), 5) for q in (10, 90)],
+        "partial_kernel_ms_p10_p90": [round(float(np.percentile(head["partial_ms_repeats"], q)), 5)
+                                      for q in (10, 90)],
         "calls_per_s": round(1e3 / ms, 1),
         "ms_per_call_mall_warm": round(head["full_ms_mall_warm"], 5),
         "partial_kernel_ms": round(part_ms, 5),
