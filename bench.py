@@ -184,6 +184,25 @@ def measure(name, steps, warmup, nsplit=0, stages=("full", "partial"), repeats=3
     return res
 
 
+def cpu_baseline_1thread(names=("c1_tiny", "c2_tp_share")):
+    """The oracle on one host thread, whole calls of the two small configurations
+    (seconds per call, median of 3)."""
+    import oracle
+    from synthetic import inputs
+    orc = oracle.load()
+    res = {}
+    for name in names:
+        wl = inputs.config(name)
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            orc.run(wl, nthreads=1)
+            times.append(time.perf_counter() - t0)
+        res[name] = {"s_per_call": round(statistics.median(times), 4),
+                     "gbs": round(algorithmic_bytes(wl) / statistics.median(times) / 1e9, 4)}
+    return res
+
+
 def gemm_reference(n=8192, reps=20):
     """Sustained bf16 matrix rate of the library GEMM (torch.matmul, n x n x n, fp32
     accumulate) on operands drawn like the workload's (one factor N(0,1), the other
@@ -499,6 +518,7 @@ def main():
         cb = cpu_baseline(args.workload)
         line["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                 for k, v in cb.items() if k != "s_per_call"}
+        line["cpu_baseline_1thread"] = cpu_baseline_1thread()
     print(json.dumps(line))
 
 
