@@ -106,7 +106,7 @@ def test_edge_shapes(orc, case):
     check_full(orc, small(**case))
 
 
-@pytest.mark.parametrize("B", [70, 130])
+@pytest.mark.parametrize("B", [70, 130, 1000])
 def test_many_sequences(orc, B):
     """More sequences than one 64-lane scan covers: the split location and the
     combine's sequence lookup take their multi-pass path."""
