@@ -320,7 +320,7 @@ def summarize(args):
     fb = fetch["FETCH_SIZE"] * 1024 * f_scale
     wb = write["WRITE_SIZE"] * 1024 * w_scale
     out = {
-        "kernel": "verify_attn_partial_kernel", "workload": "c4a_long_scattered",
+        "kernel": "verify_attn_partial_kernel", "workload": args.workload,
         "kernel_source_sha256_16": kernel_source_digest(),
         "fetch_kib_per_dispatch": fetch["FETCH_SIZE"], "write_kib_per_dispatch": write["WRITE_SIZE"],
         "dispatches": [nf.get("FETCH_SIZE"), nw.get("WRITE_SIZE")],
