@@ -202,6 +202,20 @@ def _check_workspace(workspace):
         raise ValueError("workspace must be a contiguous device tensor")
 
 
+def _check_device(stream, *tensors):
+    """All tensors on one device, the one the kernels are launched on (that of
+    `stream`, else the current device): a pointer into another GPU's memory would
+    be dereferenced as if it were local."""
+    import torch
+    devs = {t.device for t in tensors}
+    if len(devs) != 1:
+        raise ValueError(f"the tensors are on {sorted(str(d) for d in devs)}: they must share one device")
+    dev = devs.pop()
+    run = stream.device if stream is not None else torch.device("cuda", torch.cuda.current_device())
+    if dev != run:
+        raise ValueError(f"the tensors are on {dev} but the kernels would run on {run}")
+
+
 def params_for(q, kv_pool, slot_idx, *, max_seq_len: int, sm_scale: float, nsplit: int = 0,
                page_size: int = 1) -> Params:
     """Params of a call on these tensors. max_seq_len is host-known by the caller."""
@@ -218,6 +232,7 @@ def verify_attn(q, kv_pool, slot_idx, seq_lens, tree_parent, out, workspace, par
     _check_sizes(params, q=q, kv_pool=kv_pool, slot_idx=slot_idx, seq_lens=seq_lens,
                  tree_parent=tree_parent, out=out)
     _check_workspace(workspace)
+    _check_device(stream, q, kv_pool, slot_idx, seq_lens, tree_parent, out, workspace)
     _check(load_library().verify_attn(
         ctypes.byref(params), _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
         _ptr(tree_parent), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -236,6 +251,7 @@ def verify_attn_f32(q, kv_pool, slot_idx, seq_lens, tree_parent, out, workspace,
     _check_sizes(params, q=q, kv_pool=kv_pool, slot_idx=slot_idx, seq_lens=seq_lens,
                  tree_parent=tree_parent, out=out)
     _check_workspace(workspace)
+    _check_device(stream, q, kv_pool, slot_idx, seq_lens, tree_parent, out, workspace)
     _check(load_library().verify_attn_f32(
         ctypes.byref(params), _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
         _ptr(tree_parent), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -259,6 +275,7 @@ def verify_attn_debug_validate(slot_idx, seq_lens, tree_parent, params: Params, 
         flags = torch.empty(1, dtype=torch.int32, device=slot_idx.device)
     elif not flags.is_cuda or flags.dtype != torch.int32 or flags.numel() < 1:
         raise ValueError("flags must be an int32 device tensor of at least one element")
+    _check_device(stream, slot_idx, seq_lens, tree_parent, flags)
     _check(load_library().verify_attn_debug_validate(
         ctypes.byref(params), _ptr(slot_idx), _ptr(seq_lens), _ptr(tree_parent), _ptr(flags),
         _stream(stream)))
@@ -271,6 +288,7 @@ def verify_attn_partial(q, kv_pool, slot_idx, seq_lens, tree_parent, workspace, 
     _check_sizes(params, q=q, kv_pool=kv_pool, slot_idx=slot_idx, seq_lens=seq_lens,
                  tree_parent=tree_parent)
     _check_workspace(workspace)
+    _check_device(stream, q, kv_pool, slot_idx, seq_lens, tree_parent, workspace)
     _check(load_library().verify_attn_partial(
         ctypes.byref(params), _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
         _ptr(tree_parent), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -286,6 +304,7 @@ def verify_attn_combine(seq_lens, out, workspace, params: Params, stream=None) -
         raise ValueError("seq_lens must be int32 and out bfloat16")
     _check_sizes(params, seq_lens=seq_lens, out=out)
     _check_workspace(workspace)
+    _check_device(stream, seq_lens, out, workspace)
     _check(load_library().verify_attn_combine(
         ctypes.byref(params), _ptr(seq_lens), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -307,6 +326,7 @@ def verify_attn_append_kv(kv_new, slot_idx, seq_lens, kv_pool, params: Params, s
     if kv_pool.dim() != 2 or kv_pool.shape[1] != KV_DIM:
         raise ValueError("kv_pool must be [slots, 576]")
     _check_sizes(params, kv_pool=kv_pool, slot_idx=slot_idx, seq_lens=seq_lens)
+    _check_device(stream, kv_new, slot_idx, seq_lens, kv_pool)
     _check(load_library().verify_attn_append_kv(
         ctypes.byref(params), _ptr(kv_new), _ptr(slot_idx), _ptr(seq_lens), _ptr(kv_pool),
         _stream(stream)))
@@ -323,6 +343,7 @@ def verify_attn_compact_kv(kv_pool, slot_idx, kv_dst, params: Params, stream=Non
     if tuple(kv_dst.shape) != (int(params.total_kv), KV_DIM) or kv_pool.dim() != 2 or kv_pool.shape[1] != KV_DIM:
         raise ValueError("kv_dst must be [total_kv, 576] and kv_pool [slots, 576]")
     _check_sizes(params, kv_pool=kv_pool, slot_idx=slot_idx)
+    _check_device(stream, kv_pool, slot_idx, kv_dst)
     _check(load_library().verify_attn_compact_kv(
         ctypes.byref(params), _ptr(kv_pool), _ptr(slot_idx), _ptr(kv_dst), _stream(stream)))
 

@@ -259,3 +259,21 @@ def test_one_hip_runtime_whatever_the_import_order():
                          cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert out.returncode == 0, out.stderr[-2000:]
     assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
+
+
+def test_binding_refuses_tensors_on_another_device():
+    """The binding's device check, as host logic (stand-in tensors and stream): tensors on
+    two devices, or on a device other than the launch stream's, are refused before any
+    pointer reaches the library."""
+    import types
+    import torch
+    from mla_tree_verify_latent_amd import _check_device
+    d0, d1 = torch.device("cuda", 0), torch.device("cuda", 1)
+    def t(d):
+        return types.SimpleNamespace(device=d)
+    s0 = types.SimpleNamespace(device=d0)
+    _check_device(s0, t(d0), t(d0), t(d0))
+    with pytest.raises(ValueError, match="share one device"):
+        _check_device(s0, t(d0), t(d1))
+    with pytest.raises(ValueError, match="would run on"):
+        _check_device(s0, t(d1), t(d1))
