@@ -90,6 +90,15 @@ def test_e1_full_head_65k_sampled(orc):
     check_sampled(orc, inputs.config("e1_h64_65k"), n_per_seq=32)
 
 
+def test_million_key_context_sampled(orc):
+    """One sequence of a million cached keys (H=8, T=64, scattered over a 1.1M-slot
+    pool): 64 splits of 15,648 keys (489 tiles each), so the running maximum, the lazy
+    rescale and the fp32 sums carry over long runs of tiles."""
+    wl = inputs.make_workload("long_1m", B=1, H=8, T=64, prefixes=[1_000_000],
+                              pool_slots=1_100_000, seed=61)
+    check_sampled(orc, wl, n_per_seq=24)
+
+
 # ------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("case", [
