@@ -133,7 +133,16 @@ int verify_attn_combine(const verify_attn_params* p, const int32_t* seq_lens, vo
 
 /*
  * The launch decomposition chosen for these params (informational; the same
- * values the calls use). Returns a status code.
+ * values the calls use). The work is split over the KV positions of each
+ * sequence; a split's keys are processed in tiles of keys_per_tile, with one
+ * running softmax maximum per query row and split. Returns a status code.
+ *
+ * The decomposition depends on the device: its compute units (one partial
+ * workgroup each per round) and its XCDs (workgroups are dealt to them
+ * round-robin). verify_attn_plan, verify_attn_workspace_size and the calls
+ * plan for the current device (read once per device: multiProcessorCount,
+ * which is smaller under a CU-partitioned mode, and the XCD count); without a
+ * current device, for a whole MI355X (256 compute units in 8 XCDs).
  */
 typedef struct verify_attn_plan_info {
   int32_t rows_per_tile;   /* query rows (of H*T) per workgroup */
@@ -143,10 +152,20 @@ typedef struct verify_attn_plan_info {
   int32_t partial_blocks;  /* workgroups of the partial kernel */
   int32_t combine_blocks;  /* workgroups of the combine kernel */
   int32_t threads_per_block;
-  int32_t reserved;
+  int32_t keys_per_tile;   /* KV positions per tile of the partial kernel */
 } verify_attn_plan_info;
 
 int verify_attn_plan(const verify_attn_params* p, verify_attn_plan_info* info);
+
+/*
+ * The same for either input type (fp32_inputs != 0: verify_attn_f32) and an
+ * explicit device shape: num_cus compute units in num_xcds XCDs (1 <= num_xcds
+ * <= num_cus <= 65536), or the current device's when both are 0. Host only:
+ * touches no device memory. Returns a status code (VERIFY_ATTN_ERR_BAD_DIM
+ * for an invalid shape).
+ */
+int verify_attn_plan_for(const verify_attn_params* p, int32_t fp32_inputs, int32_t num_cus, int32_t num_xcds,
+                         verify_attn_plan_info* info);
 
 /*
  * Draft-row KV append: the step right before verify in the extend layout,
@@ -226,10 +245,11 @@ int verify_attn_debug_validate(const verify_attn_params* p, const int32_t* slot_
 const char* verify_attn_strerror(int status);
 
 /* ABI version of this header: (major << 16) | minor (minor 1: verify_attn_append_kv; 2: verify_attn_compact_kv;
-   3: verify_attn_f32; 4: verify_attn_debug_validate). */
+   3: verify_attn_f32; 4: verify_attn_debug_validate; 5: verify_attn_plan_for, keys_per_tile in
+   verify_attn_plan_info, plans for the current device's compute units and XCDs). */
 int verify_attn_version(void);
 
-#define VERIFY_ATTN_VERSION ((1 << 16) | 4)
+#define VERIFY_ATTN_VERSION ((1 << 16) | 5)
 
 #ifdef __cplusplus
 }

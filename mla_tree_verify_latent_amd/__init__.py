@@ -10,7 +10,7 @@ Entry points mirror the C ABI declared in ``include/verify_attn.h``:
 ``verify_attn``, ``verify_attn_partial``, ``verify_attn_combine``,
 ``verify_attn_append_kv``, ``verify_attn_compact_kv``, ``verify_attn_f32``,
 ``verify_attn_f32_workspace_size``, ``verify_attn_debug_validate``, ``verify_attn_workspace_size``, ``verify_attn_plan``,
-``verify_attn_strerror``, ``verify_attn_version``.
+``verify_attn_plan_for``, ``verify_attn_strerror``, ``verify_attn_version``.
 """
 from __future__ import annotations
 
@@ -30,7 +30,7 @@ EXPORTS = (
     "verify_attn_compact_kv", "verify_attn_f32", "verify_attn_f32_workspace_size",
     "verify_attn_debug_validate",
     "verify_attn_workspace_size",
-    "verify_attn_plan", "verify_attn_strerror", "verify_attn_version",
+    "verify_attn_plan", "verify_attn_plan_for", "verify_attn_strerror", "verify_attn_version",
 )
 
 
@@ -51,7 +51,7 @@ class PlanInfo(ctypes.Structure):
         ("rows_per_tile", ctypes.c_int32), ("row_tiles", ctypes.c_int32),
         ("keys_per_split", ctypes.c_int32), ("max_splits", ctypes.c_int32),
         ("partial_blocks", ctypes.c_int32), ("combine_blocks", ctypes.c_int32),
-        ("threads_per_block", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("threads_per_block", ctypes.c_int32), ("keys_per_tile", ctypes.c_int32),
     ]
 
 
@@ -98,6 +98,9 @@ def load_library(path: str = LIB_PATH):
     lib.verify_attn_compact_kv.restype = ctypes.c_int
     lib.verify_attn_plan.argtypes = [P, ctypes.POINTER(PlanInfo)]
     lib.verify_attn_plan.restype = ctypes.c_int
+    lib.verify_attn_plan_for.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.POINTER(PlanInfo)]
+    lib.verify_attn_plan_for.restype = ctypes.c_int
     lib.verify_attn_strerror.argtypes = [ctypes.c_int]
     lib.verify_attn_strerror.restype = ctypes.c_char_p
     lib.verify_attn_version.argtypes = []
@@ -127,9 +130,20 @@ def verify_attn_workspace_size(params: Params) -> int:
 
 
 def verify_attn_plan(params: Params) -> dict:
+    """The launch decomposition for the current device (see verify_attn_plan_info)."""
     info = PlanInfo()
     _check(load_library().verify_attn_plan(ctypes.byref(params), ctypes.byref(info)))
-    return {name: getattr(info, name) for name, _ in PlanInfo._fields_ if name != "reserved"}
+    return {name: getattr(info, name) for name, _ in PlanInfo._fields_}
+
+
+def verify_attn_plan_for(params: Params, fp32_inputs: bool = False, num_cus: int = 0,
+                         num_xcds: int = 0) -> dict:
+    """The decomposition for either input type and an explicit device shape
+    (num_cus compute units in num_xcds XCDs; both 0 = the current device)."""
+    info = PlanInfo()
+    _check(load_library().verify_attn_plan_for(ctypes.byref(params), int(bool(fp32_inputs)), int(num_cus),
+                                               int(num_xcds), ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in PlanInfo._fields_}
 
 
 def _check(status: int):

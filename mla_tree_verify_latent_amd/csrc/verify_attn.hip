@@ -74,6 +74,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct Plan {
   int M;               // H*T rows per sequence
+  int nxcd;            // XCDs the workgroups are dealt over
+  int rows_per_tile;   // query rows per partial workgroup
+  int nk;              // keys per KV tile of the partial kernel
   int row_tiles;       // ceil(M / ROWS_PER_TILE)
   int chunk;           // keys per split (multiple of NK)
   int max_splits;      // bound on the total number of splits
@@ -95,6 +98,7 @@ struct PartialArgs {
   float* part_ml;  // [max_splits][M][2] = (running max (base 2, scaled), running sum)
   int B, H, T, M;
   int row_tiles, chunk, max_splits, max_seq_len;
+  int nxcd;  // XCDs of the device (workgroup ids are dealt to them round-robin)
   int64_t total_kv, pool_slots;
   float qk_scale_log2;  // sm_scale * log2(e)
 };
@@ -198,20 +202,21 @@ __device__ int count_splits(const int32_t* __restrict__ seq_lens, int B, int T, 
 }
 
 // Work item of a partial-kernel workgroup. Items are (split, row tile) pairs
-// over the splits of all sequences; workgroup ids are dealt to the 8 XCDs
-// round-robin, so each XCD gets a contiguous, equal share of the items that
-// exist for these sequence lengths (the row tiles of one split then share that
-// XCD's L2 for their KV reads). For B <= 64 one load of seq_lens serves both
-// the item count and the split's location; larger batches scan twice.
+// over the splits of all sequences; the hardware deals workgroup ids to the
+// device's nxcd XCDs round-robin, and each XCD gets a contiguous, equal share
+// of the items that exist for these sequence lengths (the row tiles of one
+// split then share that XCD's L2 for their KV reads). For B <= 64 one load of
+// seq_lens serves both the item count and the split's location; larger
+// batches scan twice.
 __device__ bool locate_item(const int32_t* __restrict__ seq_lens, int B, int T, int max_len, int chunk,
-                            int max_splits, int row_tiles, int* g_out, int* rt_out, SplitLoc* loc) {
+                            int max_splits, int row_tiles, int nxcd, int* g_out, int* rt_out, SplitLoc* loc) {
   const int lane = threadIdx.x & 63;
   if (B > 64) {
     int n_items = count_splits(seq_lens, B, T, max_len, chunk);
     n_items = __builtin_amdgcn_readfirstlane(min(n_items, max_splits) * row_tiles);
-    const int per_xcd = (n_items + 7) >> 3;
-    const int k_on_xcd = blockIdx.x >> 3;
-    const int logical = (blockIdx.x & 7) * per_xcd + k_on_xcd;
+    const int per_xcd = (n_items + nxcd - 1) / nxcd;
+    const int k_on_xcd = blockIdx.x / nxcd;
+    const int logical = (blockIdx.x - k_on_xcd * nxcd) * per_xcd + k_on_xcd;
     if (k_on_xcd >= per_xcd || logical >= n_items) return false;
     *g_out = logical / row_tiles;
     *rt_out = logical - *g_out * row_tiles;
@@ -234,9 +239,9 @@ __device__ bool locate_item(const int32_t* __restrict__ seq_lens, int B, int T, 
     }
   }
   const int n_items = __builtin_amdgcn_readfirstlane(min(__shfl(ns_inc, 63), max_splits) * row_tiles);
-  const int per_xcd = (n_items + 7) >> 3;
-  const int k_on_xcd = blockIdx.x >> 3;
-  const int logical = (blockIdx.x & 7) * per_xcd + k_on_xcd;
+  const int per_xcd = (n_items + nxcd - 1) / nxcd;
+  const int k_on_xcd = blockIdx.x / nxcd;
+  const int logical = (blockIdx.x - k_on_xcd * nxcd) * per_xcd + k_on_xcd;
   if (k_on_xcd >= per_xcd || logical >= n_items) return false;
   const int g = logical / row_tiles;
   const int ns_first = ns_inc - ns;
@@ -422,7 +427,7 @@ void verify_attn_partial_kernel(PartialArgs a) {
 
   int g, rt;
   SplitLoc loc;
-  if (!locate_item(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, a.max_splits, a.row_tiles, &g, &rt, &loc)) return;
+  if (!locate_item(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, a.max_splits, a.row_tiles, a.nxcd, &g, &rt, &loc)) return;
   g = __builtin_amdgcn_readfirstlane(g);
   rt = __builtin_amdgcn_readfirstlane(rt);
   loc.b = __builtin_amdgcn_readfirstlane(loc.b);
@@ -839,6 +844,7 @@ struct PartialF32Args {
   float* part_ml;
   int B, H, T, M;
   int row_tiles, chunk, max_splits, max_seq_len;
+  int nxcd;
   int64_t total_kv, pool_slots;
   float qk_scale_log2;
 };
@@ -869,7 +875,7 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int g, rt;
   SplitLoc loc;
-  if (!locate_item(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, a.max_splits, a.row_tiles, &g, &rt, &loc)) return;
+  if (!locate_item(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, a.max_splits, a.row_tiles, a.nxcd, &g, &rt, &loc)) return;
   g = __builtin_amdgcn_readfirstlane(g);
   rt = __builtin_amdgcn_readfirstlane(rt);
   loc.b = __builtin_amdgcn_readfirstlane(loc.b);
@@ -1302,9 +1308,10 @@ __global__ __launch_bounds__(256) void verify_attn_validate_kernel(ValidateArgs 
 
 // ------------------------------------------------------------------- host
 
-constexpr int NUM_CUS = 256;        // MI355X compute units (one partial workgroup each)
+constexpr int MI355X_CUS = 256;     // compute units of a whole MI355X (the plan's default)
+constexpr int MI355X_XCDS = 8;      // and its XCDs
 constexpr int MIN_CHUNK = 256;      // keys per split below which partials dominate
-constexpr int64_t COMBINE_WAVES = 4096;  // combine waves resident at once (16 per CU)
+constexpr int64_t COMBINE_WAVES_PER_CU = 16;  // combine waves resident at once per CU
 constexpr int64_t ROUND_COST_TILES = 4;  // fixed cost of a round of workgroups, in tiles
 
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1323,9 +1330,39 @@ int validate(const verify_attn_params* p) {
   return VERIFY_ATTN_OK;
 }
 
-int make_plan(const verify_attn_params* p, Plan* pl, int rows_per_tile = ROWS_PER_TILE, int nk = NK) {
+// Compute units and XCDs the launch is planned for.
+struct DevShape {
+  int cus, xcds;
+};
+
+// The shape of the current device (its multiProcessorCount: fewer than 256
+// under a CU-partitioned mode, and its XCD count), read once per device id and
+// cached (thread-safe: a cache entry only ever goes from unknown to a fixed
+// value). Without a current device, a whole MI355X.
+DevShape current_shape() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return {MI355X_CUS, MI355X_XCDS};
+  static long long cache[64];  // 0 unknown, else (cus << 16) | xcds
+  long long c = __atomic_load_n(&cache[dev], __ATOMIC_ACQUIRE);
+  if (!c) {
+    int cus = 0, xcds = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      return {MI355X_CUS, MI355X_XCDS};
+    if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds < 1 ||
+        xcds > cus)
+      xcds = 1;
+    c = ((long long)cus << 16) | xcds;
+    __atomic_store_n(&cache[dev], c, __ATOMIC_RELEASE);
+  }
+  return {(int)(c >> 16), (int)(c & 0xffff)};
+}
+
+int make_plan(const verify_attn_params* p, Plan* pl, DevShape dv, int rows_per_tile = ROWS_PER_TILE,
+              int nk = NK) {
   const int rc = validate(p);
   if (rc) return rc;
+  if (dv.cus < 1 || dv.xcds < 1 || dv.xcds > dv.cus || dv.cus > (1 << 16)) return VERIFY_ATTN_ERR_BAD_DIM;
+  const int64_t NUM_CUS = dv.cus;
   const int64_t M = (int64_t)p->num_heads * p->tree_size;
   const int64_t row_tiles = ceil_div64(M, rows_per_tile);
   int64_t chunk;
@@ -1366,13 +1403,14 @@ int make_plan(const verify_attn_params* p, Plan* pl, int rows_per_tile = ROWS_PE
   const int64_t len_cap = ceil_div64(p->max_seq_len, nk) * nk;
   if (chunk > len_cap) chunk = len_cap;
   const int64_t max_splits = ceil_div64(p->total_kv, chunk) + p->num_seqs;
-  const int64_t blocks = ceil_div64(max_splits * row_tiles, 8) * 8;
+  const int64_t blocks = ceil_div64(max_splits * row_tiles, dv.xcds) * dv.xcds;
   // Combine: waves per row (a power of two up to 16, no more than the row's
   // splits) so that all rows' waves fit in about one round of the chip
   // (COMBINE_WAVES), each wave taking its splits in batches of COMBINE_BATCH.
   const int64_t rows = (int64_t)p->num_seqs * M;
   const int64_t seq_splits = ceil_div64(p->max_seq_len, chunk);
   int wpr = 1;
+  const int64_t COMBINE_WAVES = COMBINE_WAVES_PER_CU * NUM_CUS;
   while (wpr < 16 && rows * wpr * 2 <= COMBINE_WAVES && wpr * 2 <= seq_splits) wpr *= 2;
   // Few rows: split the features of a row over two workgroups, so that more
   // CUs read the partials.
@@ -1381,6 +1419,9 @@ int make_plan(const verify_attn_params* p, Plan* pl, int rows_per_tile = ROWS_PE
   if (blocks > INT32_MAX || cblocks > INT32_MAX || max_splits > INT32_MAX || chunk > INT32_MAX)
     return VERIFY_ATTN_ERR_BAD_DIM;
   pl->M = (int)M;
+  pl->nxcd = dv.xcds;
+  pl->rows_per_tile = rows_per_tile;
+  pl->nk = nk;
   pl->row_tiles = (int)row_tiles;
   pl->chunk = (int)chunk;
   pl->max_splits = (int)max_splits;
@@ -1431,6 +1472,7 @@ int launch_partial(const verify_attn_params* p, const Plan& pl, const void* q, c
   a.chunk = pl.chunk;
   a.max_splits = pl.max_splits;
   a.max_seq_len = p->max_seq_len;
+  a.nxcd = pl.nxcd;
   a.total_kv = p->total_kv;
   a.pool_slots = p->pool_slots;
   a.qk_scale_log2 = p->sm_scale * 1.4426950408889634f;
@@ -1496,6 +1538,7 @@ int launch_partial_f32(const verify_attn_params* p, const Plan& pl, const float*
   a.chunk = pl.chunk;
   a.max_splits = pl.max_splits;
   a.max_seq_len = p->max_seq_len;
+  a.nxcd = pl.nxcd;
   a.total_kv = p->total_kv;
   a.pool_slots = p->pool_slots;
   a.qk_scale_log2 = p->sm_scale * 1.4426950408889634f;
@@ -1506,7 +1549,7 @@ int launch_partial_f32(const verify_attn_params* p, const Plan& pl, const float*
 int check_partial_args(const verify_attn_params* p, Plan* pl, const void* q, const void* kv_pool,
                        const int32_t* slot_idx, const int32_t* seq_lens, const int32_t* tree_parent,
                        void* workspace, size_t workspace_bytes) {
-  const int rc = make_plan(p, pl);
+  const int rc = make_plan(p, pl, current_shape());
   if (rc) return rc;
   if (!q || !kv_pool || !slot_idx || !seq_lens || !tree_parent || !workspace) return VERIFY_ATTN_ERR_NULL_PTR;
   if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(workspace)) return VERIFY_ATTN_ERR_MISALIGNED;
@@ -1518,7 +1561,7 @@ int check_partial_args(const verify_attn_params* p, Plan* pl, const void* q, con
 
 int check_combine_args(const verify_attn_params* p, Plan* pl, const int32_t* seq_lens, void* out,
                        void* workspace, size_t workspace_bytes) {
-  const int rc = make_plan(p, pl);
+  const int rc = make_plan(p, pl, current_shape());
   if (rc) return rc;
   if (!seq_lens || !out || !workspace) return VERIFY_ATTN_ERR_NULL_PTR;
   if (!aligned16(out) || !aligned16(workspace) || ((uintptr_t)seq_lens & 3u)) return VERIFY_ATTN_ERR_MISALIGNED;
@@ -1532,23 +1575,30 @@ extern "C" {
 
 size_t verify_attn_workspace_size(const verify_attn_params* p) {
   Plan pl;
-  return make_plan(p, &pl) == VERIFY_ATTN_OK ? pl.ws_bytes : 0;
+  return make_plan(p, &pl, current_shape()) == VERIFY_ATTN_OK ? pl.ws_bytes : 0;
 }
 
-int verify_attn_plan(const verify_attn_params* p, verify_attn_plan_info* info) {
+int verify_attn_plan_for(const verify_attn_params* p, int32_t fp32_inputs, int32_t num_cus, int32_t num_xcds,
+                         verify_attn_plan_info* info) {
   if (!info) return VERIFY_ATTN_ERR_NULL_PTR;
+  DevShape dv = current_shape();
+  if (num_cus != 0 || num_xcds != 0) dv = DevShape{num_cus, num_xcds};
   Plan pl;
-  const int rc = make_plan(p, &pl);
+  const int rc = fp32_inputs ? make_plan(p, &pl, dv, F_ROWS_PER_TILE, F_NK) : make_plan(p, &pl, dv);
   if (rc) return rc;
-  info->rows_per_tile = ROWS_PER_TILE;
+  info->rows_per_tile = pl.rows_per_tile;
   info->row_tiles = pl.row_tiles;
   info->keys_per_split = pl.chunk;
   info->max_splits = pl.max_splits;
   info->partial_blocks = pl.partial_blocks;
   info->combine_blocks = pl.combine_blocks;
   info->threads_per_block = NWAVES * 64;
-  info->reserved = 0;
+  info->keys_per_tile = pl.nk;
   return VERIFY_ATTN_OK;
+}
+
+int verify_attn_plan(const verify_attn_params* p, verify_attn_plan_info* info) {
+  return verify_attn_plan_for(p, 0, 0, 0, info);
 }
 
 int verify_attn_partial(const verify_attn_params* p, const void* q, const void* kv_pool,
@@ -1587,14 +1637,14 @@ int verify_attn(const verify_attn_params* p, const void* q, const void* kv_pool,
 
 size_t verify_attn_f32_workspace_size(const verify_attn_params* p) {
   Plan pl;
-  return make_plan(p, &pl, F_ROWS_PER_TILE, F_NK) == VERIFY_ATTN_OK ? pl.ws_bytes : 0;
+  return make_plan(p, &pl, current_shape(), F_ROWS_PER_TILE, F_NK) == VERIFY_ATTN_OK ? pl.ws_bytes : 0;
 }
 
 int verify_attn_f32(const verify_attn_params* p, const float* q, const float* kv_pool, const int32_t* slot_idx,
                     const int32_t* seq_lens, const int32_t* tree_parent, float* out, void* workspace,
                     size_t workspace_bytes, void* stream) {
   Plan pl;
-  int rc = make_plan(p, &pl, F_ROWS_PER_TILE, F_NK);
+  int rc = make_plan(p, &pl, current_shape(), F_ROWS_PER_TILE, F_NK);
   if (rc) return rc;
   if (!q || !kv_pool || !slot_idx || !seq_lens || !tree_parent || !out || !workspace) return VERIFY_ATTN_ERR_NULL_PTR;
   if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out) || !aligned16(workspace)) return VERIFY_ATTN_ERR_MISALIGNED;

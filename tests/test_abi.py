@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert mtv.verify_attn_version() == (1 << 16) | 4
+    assert mtv.verify_attn_version() == (1 << 16) | 5
 
 
 def base_params(**kw):
@@ -207,6 +207,58 @@ def test_debug_validate_errors(lib):
     import torch
     if torch.cuda.device_count() == 0:
         assert lib.verify_attn_debug_validate(ctypes.byref(p), *args, None) == header_enum("VERIFY_ATTN_ERR_DEVICE")
+
+
+def _check_plan_covers(plan, lens, H, T):
+    c = plan["keys_per_split"]
+    assert c % plan["keys_per_tile"] == 0 and c > 0
+    splits = int(sum(-(-int(n) // c) for n in lens))
+    assert splits <= plan["max_splits"], plan
+    assert plan["partial_blocks"] >= plan["max_splits"] * plan["row_tiles"]
+    assert plan["row_tiles"] * plan["rows_per_tile"] >= H * T
+
+
+@pytest.mark.parametrize("cus,xcds", [(256, 8), (80, 2), (304, 8), (38, 1), (128, 4), (1, 1)])
+def test_plan_under_other_device_shapes(cus, xcds):
+    """The decomposition follows the device's compute units and XCDs: the grid is a
+    multiple of the XCD count (workgroup ids are dealt to the XCDs round-robin), the
+    automatic split length fills the given number of compute units, and every split
+    is still covered, for both input types."""
+    import numpy as np
+    rng = np.random.default_rng(cus * 31 + xcds)
+    for _ in range(60):
+        B = int(rng.integers(1, 40))
+        H = int(rng.choice([1, 8, 64]))
+        T = int(rng.integers(1, 65))
+        lens = rng.integers(T, T + int(rng.choice([1, 3000, 70000])), size=B)
+        p = mtv.make_params(num_seqs=B, num_heads=H, tree_size=T, max_seq_len=int(lens.max()),
+                            total_kv=int(lens.sum()), pool_slots=int(lens.sum()) + 1, sm_scale=0.07)
+        for f32 in (False, True):
+            plan = mtv.verify_attn_plan_for(p, f32, cus, xcds)
+            assert plan["partial_blocks"] % xcds == 0
+            _check_plan_covers(plan, lens, H, T)
+    # one long sequence at H=8, T=64: the items fill the compute units in at most two rounds
+    p = base_params()
+    plan = mtv.verify_attn_plan_for(p, False, cus, xcds)
+    items = -(-65600 // plan["keys_per_split"]) * plan["row_tiles"]
+    assert items <= 2 * max(cus, plan["row_tiles"])
+    assert items >= min(cus, 65600 // 256 * plan["row_tiles"]) * 0.75
+    if cus == 256 and xcds == 8:
+        assert plan == mtv.verify_attn_plan_for(p, False)  # no device here: a whole MI355X
+
+
+def test_plan_rejects_bad_device_shape():
+    p = base_params()
+    for cus, xcds in [(8, 16), (-1, 1), (4, 0), (1 << 17, 8)]:
+        with pytest.raises(mtv.VerifyAttnError):
+            mtv.verify_attn_plan_for(p, False, cus, xcds)
+
+
+def test_f32_plan_matches_its_workspace():
+    p = base_params()
+    plan = mtv.verify_attn_plan_for(p, True)
+    assert plan["keys_per_tile"] == 16 and plan["rows_per_tile"] == 64
+    assert mtv.verify_attn_f32_workspace_size(p) == plan["max_splits"] * 8 * 64 * (512 + 2) * 4
 
 
 def test_plan_covers_every_split():
