@@ -70,7 +70,8 @@ enum verify_attn_status {
   VERIFY_ATTN_ERR_LAUNCH_FAILED = -6,       /* the HIP runtime rejected a kernel launch */
   VERIFY_ATTN_ERR_BAD_SEQ = -7,             /* max_seq_len < tree_size, total_kv < B*T, ... */
   VERIFY_ATTN_ERR_BAD_SPLIT = -8,           /* nsplit < 0 */
-  VERIFY_ATTN_ERR_DEVICE = -9               /* no device, or the device is not gfx950 */
+  VERIFY_ATTN_ERR_DEVICE = -9,              /* no device, or the device is not gfx950 */
+  VERIFY_ATTN_ERR_SCRATCH_TOO_SMALL = -10   /* verify_attn_noalloc: partials exceed its scratch */
 };
 
 /*
@@ -116,6 +117,31 @@ size_t verify_attn_workspace_size(const verify_attn_params* p);
 int verify_attn(const verify_attn_params* p, const void* q, const void* kv_pool,
                 const int32_t* slot_idx, const int32_t* seq_lens, const int32_t* tree_parent,
                 void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * verify_attn without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture that may not call hipMalloc,
+ * tight serving loops, harnesses that forbid allocation). The split-K partials
+ * go to a scratch array inside the library instead: VERIFY_ATTN_NOALLOC_SCRATCH_BYTES
+ * of device memory per GPU, reserved when the library's code is loaded on that
+ * GPU and held until the process ends. Same arguments, layouts and result as
+ * verify_attn (the same plan and kernels, so the same bits). Makes no
+ * allocation and no host synchronisation; the scratch address is looked up
+ * once per device, at the first call on it.
+ *   Limit: calls whose verify_attn_workspace_size(p) exceeds the scratch
+ *   return VERIFY_ATTN_ERR_SCRATCH_TOO_SMALL and enqueue nothing. One split
+ *   round over the device's compute units fits (e.g. H=8, T=64 or H=64, T=64
+ *   at 65k tokens: 64.25 MiB); ragged batches needing several rounds may not.
+ *   Sharing: every call on a GPU uses that GPU's one scratch array, which
+ *   keeps the last call's contents (nothing in it needs clearing: each call
+ *   writes every partial it reads). Calls that may overlap on one GPU (other
+ *   streams, other threads) race on it and give wrong results; order them on
+ *   one stream, or use verify_attn with distinct workspaces.
+ */
+#define VERIFY_ATTN_NOALLOC_SCRATCH_BYTES (80u << 20)
+int verify_attn_noalloc(const verify_attn_params* p, const void* q, const void* kv_pool,
+                        const int32_t* slot_idx, const int32_t* seq_lens, const int32_t* tree_parent,
+                        void* out, void* stream);
 
 /*
  * The two stages of verify_attn, separately (same arguments and checks).
@@ -246,10 +272,10 @@ const char* verify_attn_strerror(int status);
 
 /* ABI version of this header: (major << 16) | minor (minor 1: verify_attn_append_kv; 2: verify_attn_compact_kv;
    3: verify_attn_f32; 4: verify_attn_debug_validate; 5: verify_attn_plan_for, keys_per_tile in
-   verify_attn_plan_info, plans for the current device's compute units and XCDs). */
+   verify_attn_plan_info, plans for the current device's compute units and XCDs; 6: verify_attn_noalloc). */
 int verify_attn_version(void);
 
-#define VERIFY_ATTN_VERSION ((1 << 16) | 5)
+#define VERIFY_ATTN_VERSION ((1 << 16) | 6)
 
 #ifdef __cplusplus
 }

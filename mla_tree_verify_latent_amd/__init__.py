@@ -7,7 +7,7 @@ no fallback: if the library is missing or the device is not gfx950 the calls
 raise.
 
 Entry points mirror the C ABI declared in ``include/verify_attn.h``:
-``verify_attn``, ``verify_attn_partial``, ``verify_attn_combine``,
+``verify_attn``, ``verify_attn_noalloc``, ``verify_attn_partial``, ``verify_attn_combine``,
 ``verify_attn_append_kv``, ``verify_attn_compact_kv``, ``verify_attn_f32``,
 ``verify_attn_f32_workspace_size``, ``verify_attn_debug_validate``, ``verify_attn_workspace_size``, ``verify_attn_plan``,
 ``verify_attn_plan_for``, ``verify_attn_strerror``, ``verify_attn_version``.
@@ -26,7 +26,7 @@ V_DIM = 512
 MAX_TREE = 64
 
 EXPORTS = (
-    "verify_attn", "verify_attn_partial", "verify_attn_combine", "verify_attn_append_kv",
+    "verify_attn", "verify_attn_noalloc", "verify_attn_partial", "verify_attn_combine", "verify_attn_append_kv",
     "verify_attn_compact_kv", "verify_attn_f32", "verify_attn_f32_workspace_size",
     "verify_attn_debug_validate",
     "verify_attn_workspace_size",
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH):
     lib.verify_attn_workspace_size.restype = ctypes.c_size_t
     lib.verify_attn.argtypes = [P, vp, vp, i32p, i32p, i32p, vp, vp, ctypes.c_size_t, vp]
     lib.verify_attn.restype = ctypes.c_int
+    lib.verify_attn_noalloc.argtypes = [P, vp, vp, i32p, i32p, i32p, vp, vp]
+    lib.verify_attn_noalloc.restype = ctypes.c_int
     lib.verify_attn_f32.argtypes = [P, vp, vp, i32p, i32p, i32p, vp, vp, ctypes.c_size_t, vp]
     lib.verify_attn_f32.restype = ctypes.c_int
     lib.verify_attn_debug_validate.argtypes = [P, i32p, i32p, i32p, vp, vp]
@@ -251,6 +253,23 @@ def verify_attn(q, kv_pool, slot_idx, seq_lens, tree_parent, out, workspace, par
         ctypes.byref(params), _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
         _ptr(tree_parent), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 80 << 20  # VERIFY_ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def verify_attn_noalloc(q, kv_pool, slot_idx, seq_lens, tree_parent, out, params: Params,
+                        stream=None) -> None:
+    """verify_attn without a workspace: the split-K partials go to the library's
+    per-GPU scratch array (NOALLOC_SCRATCH_BYTES; calls needing more raise with
+    VERIFY_ATTN_ERR_SCRATCH_TOO_SMALL). Calls that overlap on one GPU race on it."""
+    _check_tensors(q, kv_pool, slot_idx, seq_lens, tree_parent, out)
+    _check_sizes(params, q=q, kv_pool=kv_pool, slot_idx=slot_idx, seq_lens=seq_lens,
+                 tree_parent=tree_parent, out=out)
+    _check_device(stream, q, kv_pool, slot_idx, seq_lens, tree_parent, out)
+    _check(load_library().verify_attn_noalloc(
+        ctypes.byref(params), _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
+        _ptr(tree_parent), _ptr(out), _stream(stream)))
 
 
 def verify_attn_f32_workspace_size(params: Params) -> int:

@@ -1569,6 +1569,31 @@ int check_combine_args(const verify_attn_params* p, Plan* pl, const int32_t* seq
   return VERIFY_ATTN_OK;
 }
 
+// Split-K partials of verify_attn_noalloc: a file-scope device array instead
+// of a caller's workspace, for callers that cannot allocate device memory.
+// Each device holds its own copy from the library's load until the process
+// ends. Host code never passes `scratch` itself to a kernel (in host code the
+// name is a host-side stand-in, not a device address): it passes the device
+// address read once per device by scratch_ptr().
+static __device__ __align__(256) unsigned char scratch[VERIFY_ATTN_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, read with that device
+// current at the first call on it and kept per device id (thread-safe: the
+// stored address only ever goes from null to the device's fixed address).
+// Returns a status code.
+int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return VERIFY_ATTN_ERR_DEVICE;
+  static void* cache[64];
+  void* ptr = __atomic_load_n(&cache[dev], __ATOMIC_ACQUIRE);
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return VERIFY_ATTN_ERR_DEVICE;
+    __atomic_store_n(&cache[dev], ptr, __ATOMIC_RELEASE);
+  }
+  *out = ptr;
+  return VERIFY_ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1633,6 +1658,24 @@ int verify_attn(const verify_attn_params* p, const void* q, const void* kv_pool,
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if ((rc = launch_partial(p, pl, q, kv_pool, slot_idx, seq_lens, tree_parent, workspace, s))) return rc;
   return launch_combine(p, pl, seq_lens, out, workspace, s);
+}
+
+int verify_attn_noalloc(const verify_attn_params* p, const void* q, const void* kv_pool, const int32_t* slot_idx,
+                        const int32_t* seq_lens, const int32_t* tree_parent, void* out, void* stream) {
+  Plan pl;
+  int rc = make_plan(p, &pl, current_shape());
+  if (rc) return rc;
+  if (!q || !kv_pool || !slot_idx || !seq_lens || !tree_parent || !out) return VERIFY_ATTN_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out)) return VERIFY_ATTN_ERR_MISALIGNED;
+  if (((uintptr_t)slot_idx & 3u) || ((uintptr_t)seq_lens & 3u) || ((uintptr_t)tree_parent & 3u))
+    return VERIFY_ATTN_ERR_MISALIGNED;
+  if (pl.ws_bytes > VERIFY_ATTN_NOALLOC_SCRATCH_BYTES) return VERIFY_ATTN_ERR_SCRATCH_TOO_SMALL;
+  if ((rc = check_device())) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_ptr(&ws))) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((rc = launch_partial(p, pl, q, kv_pool, slot_idx, seq_lens, tree_parent, ws, s))) return rc;
+  return launch_combine(p, pl, seq_lens, out, ws, s);
 }
 
 size_t verify_attn_f32_workspace_size(const verify_attn_params* p) {
@@ -1739,6 +1782,9 @@ const char* verify_attn_strerror(int status) {
     case VERIFY_ATTN_ERR_BAD_SEQ: return "inconsistent sequence sizes (max_seq_len, total_kv)";
     case VERIFY_ATTN_ERR_BAD_SPLIT: return "nsplit must be >= 0";
     case VERIFY_ATTN_ERR_DEVICE: return "no gfx950 device is current";
+    case VERIFY_ATTN_ERR_SCRATCH_TOO_SMALL:
+      return "the call needs more split-K scratch than verify_attn_noalloc holds "
+             "(VERIFY_ATTN_NOALLOC_SCRATCH_BYTES = 80 MiB); use verify_attn with a workspace";
     default: return "unknown status";
   }
 }

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert mtv.verify_attn_version() == (1 << 16) | 5
+    assert mtv.verify_attn_version() == (1 << 16) | 6
 
 
 def base_params(**kw):
@@ -190,6 +190,33 @@ def test_f32_entry_errors(lib):
     import torch
     if torch.cuda.device_count() == 0:
         assert lib.verify_attn_f32(ctypes.byref(p), *args, n32, None) == header_enum("VERIFY_ATTN_ERR_DEVICE")
+
+
+def test_noalloc_entry_errors(lib):
+    """The allocation-free entry point validates like verify_attn, and refuses (before
+    touching a device) a call whose partials exceed its scratch array."""
+    p = base_params()
+    a = 1 << 20
+    args = [a, a, a, a, a, a]  # q, kv, slot, lens, parent, out
+    for i in range(6):
+        bad = list(args)
+        bad[i] = None
+        assert lib.verify_attn_noalloc(ctypes.byref(p), *bad, None) == header_enum("VERIFY_ATTN_ERR_NULL_PTR"), i
+    for i in (0, 1, 5):
+        bad = list(args)
+        bad[i] = a + 8
+        assert lib.verify_attn_noalloc(ctypes.byref(p), *bad, None) == header_enum("VERIFY_ATTN_ERR_MISALIGNED"), i
+    scratch = int(re.search(r"VERIFY_ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)",
+                            open(HEADER).read()).expand(r"\1 \2").split()[0]) << 20
+    assert scratch == mtv.NOALLOC_SCRATCH_BYTES
+    assert mtv.verify_attn_workspace_size(p) <= scratch  # the 64k-token H=8 shape fits
+    big = mtv.make_params(num_seqs=4, num_heads=64, tree_size=64, max_seq_len=200768, total_kv=294400,
+                          pool_slots=300000, sm_scale=0.07)
+    assert mtv.verify_attn_workspace_size(big) > scratch
+    assert lib.verify_attn_noalloc(ctypes.byref(big), *args, None) == header_enum("VERIFY_ATTN_ERR_SCRATCH_TOO_SMALL")
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert lib.verify_attn_noalloc(ctypes.byref(p), *args, None) == header_enum("VERIFY_ATTN_ERR_DEVICE")
 
 
 def test_debug_validate_errors(lib):
