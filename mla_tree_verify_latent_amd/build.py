@@ -48,16 +48,21 @@ def check_registers(extra=()) -> dict:
         }
     # bf16 kernel: 256 output accumulators; fp32 kernel: 128 (the compiler may
     # round the AGPR block up). Neither may spill.
-    need = {"verify_attn_partial_kernel": lambda n: n == 256,
-            "verify_attn_f32_partial_kernel": lambda n: n >= 128}
+    # small-row kernel: its query block (72 or 144 registers) in AGPRs.
+    need = {"verify_attn_partial_kernelE": lambda n: n == 256,
+            "verify_attn_partial_small_kernelILi1E": lambda n: n >= 72,
+            "verify_attn_partial_small_kernelILi2E": lambda n: n >= 144,
+            "verify_attn_f32_partial_kernelE": lambda n: n >= 128}
     for kname, agpr_ok in need.items():
-        found = [v for k, v in info.items() if kname + "E" in k]
+        found = [v for k, v in info.items() if kname in k]
         if len(found) != 1:
             raise RuntimeError(f"{kname} not found in the assembly metadata: {sorted(info)}")
         p = found[0]
         if p["vgpr_spill"] or p["sgpr_spill"] or not agpr_ok(p["agpr"]):
             raise RuntimeError(f"{kname} register allocation changed: {p}")
     check_mfma_hazards(text, "verify_attn_f32_partial_kernel")
+    for kernel in ("verify_attn_partial_small_kernelILi1E", "verify_attn_partial_small_kernelILi2E"):
+        check_asm_mfma_result_reads(text, kernel)
     return info
 
 
@@ -73,8 +78,11 @@ def check_mfma_hazards(text, kernel):
     """The asm MFMAs of `kernel` that accumulate in AGPRs carry no wait states
     of their own: require that none of the two instructions issued before one
     of them is a VALU instruction writing one of its source VGPRs."""
-    start = text.index(kernel)
-    body = text[text.index(":", text.index("\n" + "_Z", start - 200) + 1):]
+    # the kernel's entry label: a line "<mangled name containing `kernel`>:"
+    m = re.search(r"^(_Z\S*" + re.escape(kernel) + r"\S*):", text, flags=re.M)
+    if not m:
+        raise RuntimeError(f"{kernel}: entry label not found in the assembly")
+    body = text[m.end():]
     body = body[:body.index("s_endpgm")]
     ins = [l.split(";")[0].strip() for l in body.splitlines()]
     ins = [l for l in ins if l and not l.startswith(".") and not l.endswith(":")]
@@ -98,6 +106,37 @@ def check_mfma_hazards(text, kernel):
                 if dst & src:
                     raise RuntimeError(f"{kernel}: VALU write right before an asm MFMA source: "
                                        f"{prev!r} -> {line!r}")
+
+
+def _kernel_body(text, kernel):
+    m = re.search(r"^(_Z\S*" + re.escape(kernel) + r"\S*):", text, flags=re.M)
+    if not m:
+        raise RuntimeError(f"{kernel}: entry label not found in the assembly")
+    body = text[m.end():]
+    body = body[:body.index("s_endpgm")]
+    ins = [l.split(";")[0].strip() for l in body.splitlines()]
+    return [l for l in ins if l and not l.startswith(".") and not l.endswith(":")]
+
+
+def check_asm_mfma_result_reads(text, kernel):
+    """The QK MFMAs of the small-row kernel are asm statements (B operand in
+    AGPRs) whose VGPR results the compiler does not know to be late: require
+    that no VALU instruction reads one of their results before the next drain
+    (an 's_nop 7') or the next MFMA."""
+    ins = _kernel_body(text, kernel)
+    for i, line in enumerate(ins):
+        if not (line.startswith("v_mfma") and ", a[" in line):
+            continue
+        dst = _vregs(line.split(None, 1)[1].split(",")[0].strip())
+        for later in ins[i + 1:i + 60]:
+            if later.startswith("s_nop 7") or later.startswith("v_mfma"):
+                break
+            if later.startswith("v_") and "," in later:
+                srcs = set()
+                for tok in later.split(None, 1)[1].split(",")[1:]:
+                    srcs |= _vregs(tok.strip())
+                if srcs & dst:
+                    raise RuntimeError(f"{kernel}: {later!r} reads the result of {line!r} before a drain")
 
 
 def build(out: str = LIB, extra=()) -> str:

@@ -70,6 +70,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 struct Plan {
@@ -99,6 +100,7 @@ struct PartialArgs {
   int B, H, T, M;
   int row_tiles, chunk, max_splits, max_seq_len;
   int nxcd;  // XCDs of the device (workgroup ids are dealt to them round-robin)
+  int rows_per_tile;  // query rows per workgroup
   int64_t total_kv, pool_slots;
   float qk_scale_log2;  // sm_scale * log2(e)
 };
@@ -866,6 +868,443 @@ __device__ __forceinline__ void acc_scale4(f32x4& acc, float s) {
   }
 }
 
+// ------------------------------------------------- small-row partial kernel
+//
+// The same split-K partial results for calls with at most 32 query rows per
+// sequence (H*T <= 32: one TP8 rank's 8 heads verifying up to 4 draft tokens,
+// plain decode included; "The Commit That Locked In 6x Decode", 2. NSPLIT=64
+// for TP8 Occupancy). There the 128-row workgroup above leaves most of its
+// MFMA rows empty; here a workgroup takes the sequence's rows in one or two
+// 16-row MFMA blocks and all four waves work on every row. (The kernel also
+// runs with several row tiles of at most 32 rows sharing a split, but then
+// every compute unit gathers each key row of the split again, and the gather,
+// not the arithmetic, bounds these calls: measured slower than the 128-row
+// kernel from 40 rows up.)
+//  - QK: wave w computes the scores of keys 16w .. 16w+15 of a 64-key tile for
+//    all rows, S^T = K Q^T on MFMA 16x16x32 bf16 (A = 16 key rows from LDS,
+//    B = Q^T held in AGPRs for the whole split);
+//  - the tile's row maxima are exchanged through LDS; every wave then applies
+//    the same online-softmax update (base 2, running maximum raised only past
+//    +8) to its own keys and writes their bf16 weights to a shared LDS block;
+//  - PV: wave w accumulates output features 128w .. 128w+127 of every row over
+//    all 64 keys, O^T += V^T P^T on the same MFMA, with V^T read from the
+//    K-major tile by the LDS transpose read and P^T from the weight block.
+//    O (up to 64 fp32 per lane) stays in VGPRs and the query block (up to 144
+//    registers) in AGPRs, from which the QK MFMAs read it.
+// LDS: two 64-key tiles (72 KB each): key row k, 16-byte chunk c at
+//   (c / 8) * 8192 + k * 128 + ((c % 8) ^ sm_swz(k)) * 16,
+// sm_swz(k) = (k % 4) + 4 (((k / 4) ^ (k / 8)) % 2), a bijection of bits 0-2
+// of k when bit 3 is fixed and of bits 1 and 3 when bits 0 and 2 are fixed.
+// A 16-byte LDS read serves eight consecutive lanes per cycle; the 8-byte
+// transpose read serves the lanes of a half-wave with lane bit 2 clear, then
+// those with it set. So the QK reads (eight consecutive key rows, one chunk)
+// and the PV transpose reads (per cycle: key rows 8G + 4h + r and 8(G+1) +
+// 4h + r, r in {0, 2} or {1, 3}, two chunks each) land on distinct banks, as
+// do the weight block's writes and reads (the same swizzle by row).
+// The gather goes through VGPRs: a global load into VGPRs and an LDS write
+// move random rows at several times the rate of the direct-to-LDS load on
+// gfx950 (measured per compute unit, from L2). Wave w loads key rows 16w ..
+// 16w+15 of tile t+1 with 18 loads of 16 bytes per lane (72 VGPRs) right
+// after the barrier that frees their buffer (the top of iteration t) and
+// writes them into it after PV; the slot entries come a tile earlier.
+constexpr int SM_NK = 64;                                  // keys per tile
+constexpr int SM_ROWS = 32;                                // query rows per workgroup (at most)
+constexpr int SM_GROUP_BYTES = SM_NK * 128;                // one chunk group of the 64 rows: 8 KB
+constexpr int SM_TILE_BYTES = CHUNK_GROUPS * SM_GROUP_BYTES;  // 72 KB
+constexpr int SM_QK_STEPS = KV_DIM / 32;                   // 18 k-steps of 32 features
+constexpr int SM_FB = V_DIM / NWAVES / 16;                 // 8 output blocks of 16 features per wave
+constexpr int SM_LOADS = 2 * CHUNK_GROUPS;                 // 18 gather loads per wave and tile
+constexpr int SM_P_BYTES = SM_ROWS * SM_NK * 2;            // bf16 weights of a tile: [row][key]
+constexpr int SM_MAX_M = SM_ROWS;  // H*T up to which the plan takes this kernel (one row tile)
+constexpr int SM_LDS = 2 * SM_TILE_BYTES + SM_P_BYTES + NWAVES * SM_ROWS * 4;
+static_assert(SM_LDS + MAX_TREE * 8 <= 160 * 1024, "small-row kernel LDS");
+
+__device__ __forceinline__ int sm_swz(int k) { return (k & 3) | ((((k >> 2) ^ (k >> 3)) & 1) << 2); }
+
+// acc += a * b, MFMA 16x16x32 bf16 with the B operand (the query fragment,
+// loop-invariant) held in AGPRs and the accumulator in VGPRs: the query block
+// stays out of the VGPRs, which hold O and the gather in flight. The compiler
+// does not model an asm MFMA's latency: its accumulator is read by VALU
+// instructions only after mfma_drain_acc(); A comes from an LDS read and B is
+// never written in the loop.
+__device__ __forceinline__ void mfma16_qk(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+// The same with a zero accumulator (C is the inline constant 0, so no VALU
+// instruction writes it just before).
+__device__ __forceinline__ void mfma16_qk_first(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "a"(b));
+}
+// The wait states of mfma_drain(), taking the accumulators of the asm MFMAs
+// above as operands: a plain drain orders nothing for the compiler, which
+// would be free to move the first VALU reads of these values above it.
+template <int N>
+__device__ __forceinline__ void mfma_drain_acc(f32x4 (&acc)[N][2]) {
+  if constexpr (N == 1)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0][0]), "+v"(acc[0][1]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
+}
+
+__device__ __forceinline__ void lds_write_b128(uint32_t addr, const u32x4& v) { *(LDS_AS u32x4*)(uintptr_t)addr = v; }
+
+// NRB: 16-row MFMA blocks of query rows per workgroup (1: up to 16 rows, 2: up to 32).
+template <int NRB>
+__global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void verify_attn_partial_small_kernel(PartialArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[SM_LDS];
+  __shared__ unsigned long long anc_s[MAX_TREE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int g, rt;
+  SplitLoc loc;
+  if (!locate_item(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, a.max_splits, a.row_tiles, a.nxcd, &g, &rt, &loc)) return;
+  g = __builtin_amdgcn_readfirstlane(g);
+  rt = __builtin_amdgcn_readfirstlane(rt);
+  loc.b = __builtin_amdgcn_readfirstlane(loc.b);
+  loc.g0 = __builtin_amdgcn_readfirstlane(loc.g0);
+  loc.len = __builtin_amdgcn_readfirstlane(loc.len);
+  loc.seg = ((int64_t)__builtin_amdgcn_readfirstlane((int)(loc.seg >> 32)) << 32) |
+            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)loc.seg);
+  const int k0 = (g - loc.g0) * a.chunk;
+  const int k1 = min(k0 + a.chunk, loc.len);
+  const int P = loc.len - a.T;
+  const int ntiles = (k1 - k0 + SM_NK - 1) / SM_NK;
+
+  const uint32_t smem_base = lds_addr(smem);
+  const uint32_t p_base = smem_base + 2 * SM_TILE_BYTES;  // bf16 weights [32 rows][64 keys]
+  const uint32_t rmax_base = p_base + SM_P_BYTES;         // fp32 [32 rows][4 waves]
+  const int64_t slot_hi = a.total_kv - 1;
+  const int pool_hi = (int)(a.pool_slots - 1 < (int64_t)INT32_MAX ? a.pool_slots - 1 : (int64_t)INT32_MAX);
+
+  // Rows of this workgroup: local row lr = 16 rb + (lane % 16) is query row
+  // rt * rows_per_tile + lr of the sequence (rows past the tile or M are zero).
+  const int rpt = a.rows_per_tile;
+  const int l16 = lane & 15, grp = lane >> 4;
+  int qrow[NRB];
+  bool row_ok[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int lr = 16 * rb + l16;
+    qrow[rb] = rt * rpt + lr;
+    row_ok[rb] = lr < rpt && qrow[rb] < a.M;
+  }
+
+  // Gather rows of this lane: key rows 16 wave + 8 hh + lane / 8 of a tile,
+  // 16-byte position lane % 8 of each chunk group (keys past the split end
+  // repeat its last key).
+  auto slot_of = [&](int t, int hh) {
+    int key = k0 + t * SM_NK + wave * 16 + 8 * hh + (lane >> 3);
+    key = key < k1 ? key : k1 - 1;
+    int64_t si = loc.seg + key;
+    si = si < slot_hi ? si : slot_hi;
+    return a.slot_idx[si];
+  };
+  const int ld_elem0 = 8 * ((lane & 7) ^ sm_swz(lane >> 3));
+  const int ld_elem1 = 8 * ((lane & 7) ^ sm_swz(8 + (lane >> 3)));
+  auto gather_load = [&](int s0, int s1, u32x4 (&gv)[SM_LOADS]) {
+    s0 = s0 < 0 ? 0 : (s0 > pool_hi ? pool_hi : s0);
+    s1 = s1 < 0 ? 0 : (s1 > pool_hi ? pool_hi : s1);
+    const uint16_t* src0 = a.kv + (int64_t)s0 * KV_DIM + ld_elem0;
+    const uint16_t* src1 = a.kv + (int64_t)s1 * KV_DIM + ld_elem1;
+#pragma unroll
+    for (int j = 0; j < CHUNK_GROUPS; ++j) {
+      gv[2 * j] = *reinterpret_cast<const u32x4*>(src0 + 64 * j);
+      gv[2 * j + 1] = *reinterpret_cast<const u32x4*>(src1 + 64 * j);
+    }
+  };
+  auto gather_store = [&](int t, const u32x4 (&gv)[SM_LOADS]) {
+    const uint32_t dst = smem_base + (t & 1) * SM_TILE_BYTES + wave * 16 * 128 + 16 * lane;
+#pragma unroll
+    for (int j = 0; j < CHUNK_GROUPS; ++j) {
+      lds_write_b128(dst + j * SM_GROUP_BYTES, gv[2 * j]);
+      lds_write_b128(dst + j * SM_GROUP_BYTES + 8 * 128, gv[2 * j + 1]);
+    }
+  };
+
+  // ---- prologue, loads oldest first: slot entries of tile 0, the tree's
+  // parent pointers (wave 0), the query block, slot entries of tile 1, then
+  // the gather of tile 0 once its slot entries are in.
+  int sn0 = slot_of(0, 0), sn1 = slot_of(0, 1);
+  int parent = -1;
+  if (wave == 0) parent = a.tree_parent[(int64_t)loc.b * a.T + (lane < a.T ? lane : a.T - 1)];
+  // The query block (the workgroup's 32 local rows, 1,152 bytes each) passes
+  // through LDS, in tile 1's buffer, which is free until the end of the first
+  // iteration: wave w loads local rows 8w .. 8w+7 with nine 1 KB loads (16-byte
+  // piece s of the block holds piece (s % 72) ^ (row % 8) of row s / 72, so that
+  // the reads below, eight consecutive rows per cycle, hit distinct banks);
+  // rows past the tile read the tile's first row and are zeroed when read.
+  const uint32_t qstage = smem_base + SM_TILE_BYTES;
+  u32x4 qs[9];
+#pragma unroll
+  for (int j = 0; j < 9; ++j) {
+    const int sidx = 72 * 8 * wave + 64 * j + lane;
+    const int r = sidx / 72, pc = (sidx - 72 * r) ^ (r & 7);
+    const int gr = rt * rpt + r;
+    const int grow = (r < rpt && gr < a.M) ? gr : rt * rpt;
+    qs[j] = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)loc.b * a.M + grow) * KV_DIM + 8 * pc);
+  }
+  int sx0 = slot_of(1, 0), sx1 = slot_of(1, 1);
+  u32x4 gv[SM_LOADS];
+  gather_load(sn0, sn1, gv);
+#pragma unroll
+  for (int j = 0; j < 9; ++j) lds_write_b128(qstage + 1024 * (9 * wave + j) + 16 * lane, qs[j]);
+  gather_store(0, gv);
+  lds_barrier();  // the query block and tile 0 in LDS
+  sn0 = sx0;
+  sn1 = sx1;
+  // Query fragments (B operand of S^T = K Q^T): lane l holds local row
+  // 16 rb + l%16, features 32 ks + 8 (l/16) .. +7 (piece 4 ks + l/16).
+  bf16x8 qf[NRB][SM_QK_STEPS];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int r = 16 * rb + l16;
+#pragma unroll
+    for (int ks = 0; ks < SM_QK_STEPS; ++ks) {
+      u32x4 v = __builtin_bit_cast(u32x4, lds_read_b128(qstage + 16 * (72 * r + ((4 * ks + grp) ^ (r & 7)))));
+      if (!row_ok[rb]) v = u32x4{0u, 0u, 0u, 0u};
+      qf[rb][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  // Ancestor masks (as in verify_attn_partial_kernel).
+  if (wave == 0) {
+    int up = (parent >= 0 && parent < lane && lane < a.T) ? parent : -1;
+    unsigned long long m = lane < a.T ? (1ull << lane) : 0ull;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const int src = up >= 0 ? up : lane;
+      const unsigned long long m_up = __shfl(m, src);
+      const int up_up = __shfl(up, src);
+      if (up >= 0) {
+        m |= m_up;
+        up = up_up;
+      }
+    }
+    if (lane < a.T) anc_s[lane] = m;
+  }
+
+  // Operand read offsets inside a tile (chunk group added per step).
+  //  QK step ks: key row 16 wave + l%16, chunk 4 ks + l/16.
+  int qk_off[2];
+  {
+    const int kr = wave * 16 + l16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) qk_off[h] = kr * 128 + (((4 * h + grp) ^ sm_swz(kr)) << 4);
+  }
+  //  PV block fb, key step ks, half h: 16-lane group G = l/16, lane 4r + c of
+  //  the group addresses key row 32 ks + 8 G + 4 h + r, features
+  //  128 wave + 16 fb + 4c .. +3 (chunk 16 wave + 2 fb + c/2, 8-byte half c%2).
+  // (The swizzle of key row kr depends on kr % 16 only, so key step ks adds
+  // 32 * 128 bytes.)
+  int pv_off[2][4];  // [h][fb % 4] at ks = 0
+  {
+    const int r = l16 >> 2, c = l16 & 3;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int f4 = 0; f4 < 4; ++f4) {
+        const int kr = 8 * grp + 4 * h + r;
+        const int pos = (2 * f4 + (c >> 1)) ^ sm_swz(kr);
+        pv_off[h][f4] = kr * 128 + (pos << 4) + 8 * (c & 1);
+      }
+  }
+  // Weight block: row lr, keys 8 j .. 8 j + 7 at lr * 128 + ((j ^ sm_swz(lr)) << 4).
+  auto p_addr = [&](int lr, int j) { return p_base + lr * 128 + (((j ^ sm_swz(lr)) & 7) << 4); };
+
+  f32x4 o[SM_FB][NRB];
+#pragma unroll
+  for (int fb = 0; fb < SM_FB; ++fb)
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) o[fb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[NRB], l_run[NRB];  // running reference max of local row 16 rb + l%16, this lane's share of its sum
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+  }
+
+  for (int it = 0; it < ntiles; ++it) {
+    // The barrier publishes tile it (written by every wave at the end of the
+    // previous iteration, or in the prologue) and frees the other buffer (every
+    // wave is done with tile it-1, and, at it = 0, with the query block).
+    lds_barrier();
+    const uint32_t cur = smem_base + (it & 1) * SM_TILE_BYTES;
+    const bool more = it + 1 < ntiles;  // wave-uniform
+    if (more) {
+      gather_load(sn0, sn1, gv);  // tile it+1, written into LDS after PV
+      sx0 = slot_of(it + 2, 0);
+      sx1 = slot_of(it + 2, 1);
+    }
+
+    // ---- S^T = K Q^T for this wave's 16 keys: lane l holds row 16 rb + l%16,
+    // keys 16 wave + 4 (l/16) + i, i < 4 (two accumulators per row block, even
+    // and odd k-steps).
+    f32x4 s2[NRB][2];
+    {
+      constexpr int AHEAD = 4;
+      auto kread = [&](int ks) { return lds_read_b128(cur + (ks >> 1) * SM_GROUP_BYTES + qk_off[ks & 1]); };
+      bf16x8 kbuf[AHEAD];
+#pragma unroll
+      for (int ks = 0; ks < AHEAD; ++ks) kbuf[ks] = kread(ks);
+#pragma unroll
+      for (int ks = 0; ks < SM_QK_STEPS; ++ks) {
+        const bf16x8 kv = kbuf[ks % AHEAD];
+        if (ks + AHEAD < SM_QK_STEPS) kbuf[ks % AHEAD] = kread(ks + AHEAD);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          if (ks < 2) mfma16_qk_first(s2[rb][ks], kv, qf[rb][ks]);
+          else mfma16_qk(s2[rb][ks & 1], kv, qf[rb][ks]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    static_assert(NRB == 1 || NRB == 2, "row blocks");
+    mfma_drain_acc<NRB>(s2);  // the QK accumulators are read below
+    f32x4 s[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) s[rb] = s2[rb][0] + s2[rb][1];
+    // ---- scale, tree mask, the tile's row maxima through LDS
+    const int kt = k0 + it * SM_NK;
+    const int kb = kt + wave * 16 + 4 * grp;  // key of s[rb][0]
+    const bool edge = kt + SM_NK > k1 || kt + SM_NK > P;  // the tile reaches the split end or the tree
+    float mx[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[rb][i] *= a.qk_scale_log2;
+      if (edge) {
+        const unsigned long long anc = anc_s[row_ok[rb] ? qrow[rb] / a.H : 0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb + i;
+          const int u = key - P;
+          const bool vis = (key < k1) & ((u < 0) | (((anc >> (u & 63)) & 1ull) != 0));
+          s[rb][i] = vis ? s[rb][i] : -INFINITY;
+        }
+      }
+      float m4 = fmaxf(fmaxf(s[rb][0], s[rb][1]), fmaxf(s[rb][2], s[rb][3]));
+      m4 = fmaxf(m4, xor16(m4));  // the four lane groups hold keys of the same row
+      mx[rb] = fmaxf(m4, xor32(m4));
+    }
+    if (grp == 0) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+        *(LDS_AS float*)(uintptr_t)(rmax_base + ((16 * rb + l16) * NWAVES + wave) * 4) = mx[rb];
+    }
+    lds_barrier();
+
+    // ---- online softmax (every wave takes the same decision per row), the
+    // bf16 weights of this wave's keys into the weight block
+    bool any_raise = false;
+    float alpha[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const f32x4 wm = *(const LDS_AS f32x4*)(uintptr_t)(rmax_base + (16 * rb + l16) * NWAVES * 4);
+      const float t = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+      const bool raise = t > m_run[rb] + LAZY_RESCALE_LOG2;
+      // O needs rescaling only in rows that already hold weights
+      any_raise |= __ballot(raise & (m_run[rb] != -INFINITY)) != 0;
+      alpha[rb] = raise ? __builtin_amdgcn_exp2f(m_run[rb] - t) : 1.0f;  // m_run = -inf -> 0
+      m_run[rb] = raise ? t : m_run[rb];
+      const float mu = (m_run[rb] == -INFINITY) ? 0.f : m_run[rb];
+      bf16x4 pw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[i] = (__bf16)__builtin_amdgcn_exp2f(s[rb][i] - mu);
+      // the running sum uses the same bf16-rounded weights that enter O
+      const u32x2 pbits = __builtin_bit_cast(u32x2, pw);
+      l_run[rb] = l_run[rb] * alpha[rb] +
+                  ((__builtin_bit_cast(float, pbits[0] << 16) + __builtin_bit_cast(float, pbits[0] & 0xffff0000u)) +
+                   (__builtin_bit_cast(float, pbits[1] << 16) + __builtin_bit_cast(float, pbits[1] & 0xffff0000u)));
+      {
+        const int lr = 16 * rb + l16;
+        const int j = 2 * wave + (grp >> 1);  // 8-key piece of keys 16 wave + 4 grp
+        *(LDS_AS u32x2*)(uintptr_t)(p_addr(lr, j) + 8 * (grp & 1)) = pbits;
+      }
+    }
+    lds_barrier();
+
+    if (any_raise) {  // O (PV up to tile it-1) *= alpha of its row
+#pragma unroll
+      for (int fb = 0; fb < SM_FB; ++fb)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) o[fb][rb] *= alpha[rb];
+    }
+
+    // ---- O^T += V^T P^T: this wave's 8 feature blocks x the rows x 64 keys
+    bf16x8 pb[NRB][2];  // [rb][ks]: lane l holds row 16 rb + l%16, keys 32 ks + 8 (l/16) .. +7
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) pb[rb][ks] = lds_read_b128(p_addr(16 * rb + l16, 4 * ks + grp));
+    {
+      auto vread = [&](int st) {  // step st = 8 ks + fb
+        const int ks = st >> 3, fb = st & 7;
+        const uint32_t base = cur + (2 * wave + (fb >> 2)) * SM_GROUP_BYTES + ks * 32 * 128;
+        const bf16x4 v0 = lds_read_tr(base + pv_off[0][fb & 3]);
+        const bf16x4 v1 = lds_read_tr(base + pv_off[1][fb & 3]);
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      constexpr int AHEAD = 4;
+      bf16x8 vbuf[AHEAD];
+#pragma unroll
+      for (int st = 0; st < AHEAD; ++st) vbuf[st] = vread(st);
+#pragma unroll
+      for (int st = 0; st < 2 * SM_FB; ++st) {
+        const bf16x8 vt = vbuf[st % AHEAD];
+        if (st + AHEAD < 2 * SM_FB) vbuf[st % AHEAD] = vread(st + AHEAD);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          o[st & 7][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb[rb][st >> 3], o[st & 7][rb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (more) {
+      gather_store(it + 1, gv);
+      sn0 = sx0;
+      sn1 = sx1;
+    }
+  }
+
+  // ---- partial results: the row's running sum over the four lane groups and
+  // the four waves (through the row-max buffer, free since the last barrier)
+  float lsum[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    float t = l_run[rb] + xor16(l_run[rb]);
+    lsum[rb] = t + xor32(t);
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+      *(LDS_AS float*)(uintptr_t)(rmax_base + ((16 * rb + l16) * NWAVES + wave) * 4) = lsum[rb];
+  }
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    if (!row_ok[rb]) continue;
+    const int64_t rowid = (int64_t)g * a.M + qrow[rb];
+    float* po = a.part_o + rowid * V_DIM + wave * 128 + 4 * grp;
+#pragma unroll
+    for (int fb = 0; fb < SM_FB; ++fb) *reinterpret_cast<f32x4*>(po + 16 * fb) = o[fb][rb];
+  }
+  lds_barrier();
+  if (wave == 0 && grp == 0) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      if (!row_ok[rb]) continue;
+      const f32x4 wl = *(const LDS_AS f32x4*)(uintptr_t)(rmax_base + (16 * rb + l16) * NWAVES * 4);
+      const float t = (wl[0] + wl[1]) + (wl[2] + wl[3]);
+      const int64_t rowid = (int64_t)g * a.M + qrow[rb];
+      a.part_ml[2 * rowid] = m_run[rb];
+      a.part_ml[2 * rowid + 1] = t;
+    }
+  }
+}
+
+
 __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void verify_attn_f32_partial_kernel(PartialF32Args a) {
   __shared__ __attribute__((aligned(1024))) char smem[F_NBUF * F_TILE_BYTES];
@@ -1357,13 +1796,25 @@ DevShape current_shape() {
   return {(int)(c >> 16), (int)(c & 0xffff)};
 }
 
-int make_plan(const verify_attn_params* p, Plan* pl, DevShape dv, int rows_per_tile = ROWS_PER_TILE,
-              int nk = NK) {
+// rows_per_tile = 0: the bf16 path, which takes the small-row kernel (at most
+// 32 rows per workgroup, 64-key tiles) for H*T <= SM_MAX_M and the 128-row
+// kernel otherwise; the fp32 path passes its own geometry.
+int make_plan(const verify_attn_params* p, Plan* pl, DevShape dv, int rows_per_tile = 0, int nk = NK) {
   const int rc = validate(p);
   if (rc) return rc;
   if (dv.cus < 1 || dv.xcds < 1 || dv.xcds > dv.cus || dv.cus > (1 << 16)) return VERIFY_ATTN_ERR_BAD_DIM;
   const int64_t NUM_CUS = dv.cus;
   const int64_t M = (int64_t)p->num_heads * p->tree_size;
+  if (rows_per_tile == 0) {
+    if (M <= SM_MAX_M) {
+      // the rows spread evenly over ceil(M / 32) row tiles
+      rows_per_tile = (int)ceil_div64(M, ceil_div64(M, SM_ROWS));
+      nk = SM_NK;
+    } else {
+      rows_per_tile = ROWS_PER_TILE;
+      nk = NK;
+    }
+  }
   const int64_t row_tiles = ceil_div64(M, rows_per_tile);
   int64_t chunk;
   if (p->nsplit > 0) {
@@ -1473,10 +1924,16 @@ int launch_partial(const verify_attn_params* p, const Plan& pl, const void* q, c
   a.max_splits = pl.max_splits;
   a.max_seq_len = p->max_seq_len;
   a.nxcd = pl.nxcd;
+  a.rows_per_tile = pl.rows_per_tile;
   a.total_kv = p->total_kv;
   a.pool_slots = p->pool_slots;
   a.qk_scale_log2 = p->sm_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(verify_attn_partial_kernel, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
+  if (pl.rows_per_tile <= SM_ROWS / 2)
+    hipLaunchKernelGGL(verify_attn_partial_small_kernel<1>, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
+  else if (pl.rows_per_tile <= SM_ROWS)
+    hipLaunchKernelGGL(verify_attn_partial_small_kernel<2>, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(verify_attn_partial_kernel, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
   return hipGetLastError() == hipSuccess ? VERIFY_ATTN_OK : VERIFY_ATTN_ERR_LAUNCH_FAILED;
 }
 

@@ -116,6 +116,35 @@ def test_edge_shapes(orc, case):
     check_full(orc, small(**case))
 
 
+@pytest.mark.parametrize("T", [1, 5, 9, 12])
+@pytest.mark.parametrize("H", [8, 16])
+def test_production_row_counts_full(orc, H, T):
+    """One TP rank's heads verifying a few draft tokens at a 65k-token prefix: the
+    row counts (H*T = 8 .. 192) on both sides of the small-row kernel's limit,
+    every output row compared."""
+    import mla_tree_verify_latent_amd as mtv
+    wl = inputs.make_workload(f"h{H}_t{T}_65k", B=1, H=H, T=T, prefixes=[65536], pool_slots=131072,
+                              seed=900 + 10 * H + T)
+    plan = mtv.verify_attn_plan(params_of(wl))
+    assert (plan["rows_per_tile"] <= 32) == (H * T <= 32), plan
+    check_full(orc, wl)
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=3, H=8, T=9, prefixes=[0, 4095, 70], nsplit=0),     # ragged, P = 0, a 4,104-key sequence
+    dict(B=1, H=4, T=8, prefixes=[1000], nsplit=7),            # 32 rows: two row blocks, forced splits
+    dict(B=2, H=1, T=32, prefixes=[129, 64], nsplit=0),        # 32 rows, the tree spans half a tile
+    dict(B=1, H=8, T=3, prefixes=[63], nsplit=1),              # one split, the tree crosses the first tile
+    dict(B=1, H=2, T=40, prefixes=[5000], nsplit=3, tree="chain"),
+    dict(B=1, H=16, T=2, prefixes=[200000], nsplit=0),         # 32 rows in one row tile, 200k keys
+], ids=lambda c: "B{B}_H{H}_T{T}_P{prefixes}_n{nsplit}".format(**c))
+def test_small_row_kernel_shapes(orc, case):
+    case = dict(case)
+    nsplit = case.pop("nsplit")
+    wl = small(**case, seed=40 + case["T"])
+    check_full(orc, wl, nsplit=nsplit)
+
+
 @pytest.mark.parametrize("B", [70, 130, 1000])
 def test_many_sequences(orc, B):
     """More sequences than one 64-lane scan covers: the split location and the

@@ -45,7 +45,8 @@ def _workload(shape, seed, dtype="bf16", **kw):
     if shape in inputs.CONFIGS:
         cfg = {**inputs.CONFIGS[shape], "dtype": dtype, **kw}
         return inputs.make_workload(shape, **cfg)
-    B, H, T, prefixes = dict(small=(2, 8, 16, [3000, 1200]), ragged=(3, 4, 24, [0, 2500, 700]))[shape]
+    B, H, T, prefixes = dict(small=(2, 8, 16, [3000, 1200]), ragged=(3, 4, 24, [0, 2500, 700]),
+                             few_rows=(2, 8, 4, [3000, 1200]), decode=(3, 8, 1, [4000, 0, 777]))[shape]
     return inputs.make_workload(shape, B=B, H=H, T=T, prefixes=prefixes,
                                 pool_slots=sum(prefixes) + B * T + 101, seed=seed, dtype=dtype, **kw)
 
@@ -79,8 +80,10 @@ def _check_f32(orc, wl, nsplit=0):
 # ------------------------------------------------------------ bf16 entry point
 
 @pytest.mark.parametrize("q_std", [16, 64])
-@pytest.mark.parametrize("shape", ["small", "ragged", "e2_h8_t9_65k"])
+@pytest.mark.parametrize("shape", ["small", "ragged", "few_rows", "decode", "e2_h8_t9_65k"])
 def test_peaked_queries(orc, shape, q_std):
+    if shape == "decode" and q_std == 16:
+        q_std = 32  # 8 query rows at spread 16 never overtake a running maximum by 8
     wl = _workload(shape, seed=50 + q_std, q_std=float(q_std))
     _show_rescale(wl)
     _check_bf16(orc, wl)
@@ -93,6 +96,9 @@ def test_peaked_queries(orc, shape, q_std):
     ("ragged", 60.0, 333, 5, 0),
     ("e2_h8_t9_65k", 40.0, None, 0, 0),
     ("c4a_long_scattered", 80.0, None, 0, 0),
+    ("few_rows", 60.0, None, 0, 0),        # 32 rows: the small-row kernel, one split per ramp
+    ("few_rows", 300.0, 700, 123, 0),
+    ("decode", 200.0, None, 0, 1),         # T = 1, one split of each whole sequence
 ], ids=lambda v: str(v))
 def test_score_ramp(orc, shape, amp, period, offset, nsplit):
     wl = _workload(shape, seed=70)
