@@ -131,7 +131,7 @@ int verify_attn(const verify_attn_params* p, const void* q, const void* kv_pool,
  *   Limit: calls whose verify_attn_workspace_size(p) exceeds the scratch
  *   return VERIFY_ATTN_ERR_SCRATCH_TOO_SMALL and enqueue nothing. One split
  *   round over the device's compute units fits (e.g. H=8, T=64 or H=64, T=64
- *   at 65k tokens: 64.25 MiB); ragged batches needing several rounds may not.
+ *   at 65k tokens: 32.25 MiB); ragged batches needing several rounds may not.
  *   Sharing: every call on a GPU uses that GPU's one scratch array, which
  *   keeps the last call's contents (nothing in it needs clearing: each call
  *   writes every partial it reads). Calls that may overlap on one GPU (other
@@ -145,10 +145,12 @@ int verify_attn_noalloc(const verify_attn_params* p, const void* q, const void* 
 
 /*
  * The two stages of verify_attn, separately (same arguments and checks).
- * verify_attn_partial writes the per-split softmax partials (running max,
- * running sum, unnormalised V sum) into the workspace; verify_attn_combine
- * reads them and writes `out`. verify_attn == partial followed by combine.
- * Exposed so a profiler or benchmark can time the stages on their own.
+ * verify_attn_partial writes the per-split softmax partials (running max and
+ * running sum in fp32; the split's V average, its weighted V sum divided by the
+ * running sum, rounded to bf16, nearest even) into the workspace;
+ * verify_attn_combine reads them and writes `out`.
+ * verify_attn == partial followed by combine. Exposed so a profiler or
+ * benchmark can time the stages on their own.
  */
 int verify_attn_partial(const verify_attn_params* p, const void* q, const void* kv_pool,
                         const int32_t* slot_idx, const int32_t* seq_lens,

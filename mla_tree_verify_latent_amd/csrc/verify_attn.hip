@@ -24,7 +24,11 @@
 //    with the LDS transpose read; O stays in AGPRs;
 //  - fp32 online softmax in base 2, tree mask from per-node 64-bit ancestor
 //    masks built on the device from the parent pointers;
-//  - a log-sum-exp combine kernel merges the splits and rounds to bf16.
+//  - at most 32 query rows per sequence: a small-row kernel (64-key tiles
+//    gathered through VGPRs; see its header) instead;
+//  - a split's partial result is its V average (weighted V sum over running
+//    sum) rounded to bf16, with the fp32 running maximum and sum; a
+//    log-sum-exp combine kernel merges the splits and rounds to bf16.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -95,8 +99,8 @@ struct PartialArgs {
   const int32_t* slot_idx;
   const int32_t* seq_lens;
   const int32_t* tree_parent;
-  float* part_o;   // [max_splits][M][512]
-  float* part_ml;  // [max_splits][M][2] = (running max (base 2, scaled), running sum)
+  uint16_t* part_o;  // bf16 [max_splits][M][512]: V sum / running sum, RNE
+  float* part_ml;    // [max_splits][M][2] = (running max (base 2, scaled), running sum)
   int B, H, T, M;
   int row_tiles, chunk, max_splits, max_seq_len;
   int nxcd;  // XCDs of the device (workgroup ids are dealt to them round-robin)
@@ -122,7 +126,7 @@ struct CompactArgs {
 };
 
 struct CombineArgs {
-  const float* part_o;
+  const void* part_o;  // partial V averages: bf16 (bf16 path) or fp32 (fp32-input path)
   const float* part_ml;
   const int32_t* seq_lens;
   uint16_t* out;      // bf16 output, or
@@ -377,11 +381,14 @@ __device__ __forceinline__ float xor16(float x) {
   return __builtin_bit_cast(float, ((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two floats to a pair of bf16 (round to nearest even), `lo` in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+
+// The two bf16 values of a packed pair, widened (exactly) to float.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
 // ------------------------------------------------------------ partial kernel
 //
@@ -773,14 +780,17 @@ void verify_attn_partial_kernel(PartialArgs a) {
   // ---- partial results of this split
   const float l_row = l_run + xor32(l_run);
   if (row_ok) {
+    // the split's V average (0 for a row with every key of the split masked)
+    const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
     const int64_t rowid = (int64_t)g * a.M + qrow;
-    float* po = a.part_o + rowid * V_DIM + 4 * hl;
+    uint16_t* po = a.part_o + rowid * V_DIM + 4 * hl;
 #pragma unroll
     for (int cb = 0; cb < PV_BLOCKS; ++cb)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4)
-        *reinterpret_cast<f32x4*>(po + 32 * cb + 8 * i4) =
-            f32x4{o[cb][4 * i4], o[cb][4 * i4 + 1], o[cb][4 * i4 + 2], o[cb][4 * i4 + 3]};
+        *reinterpret_cast<u32x2*>(po + 32 * cb + 8 * i4) =
+            u32x2{pack_bf16x2(o[cb][4 * i4] * inv, o[cb][4 * i4 + 1] * inv),
+                  pack_bf16x2(o[cb][4 * i4 + 2] * inv, o[cb][4 * i4 + 3] * inv)};
     if (hl == 0) {
       a.part_ml[2 * rowid] = m_run;
       a.part_ml[2 * rowid + 1] = l_row;
@@ -842,8 +852,8 @@ struct PartialF32Args {
   const int32_t* slot_idx;
   const int32_t* seq_lens;
   const int32_t* tree_parent;
-  float* part_o;
-  float* part_ml;
+  float* part_o;   // [max_splits][M][512]: V sum / running sum
+  float* part_ml;  // [max_splits][M][2] = (running max, running sum)
   int B, H, T, M;
   int row_tiles, chunk, max_splits, max_seq_len;
   int nxcd;
@@ -1270,34 +1280,28 @@ void verify_attn_partial_small_kernel(PartialArgs a) {
   }
 
   // ---- partial results: the row's running sum over the four lane groups and
-  // the four waves (through the row-max buffer, free since the last barrier)
-  float lsum[NRB];
+  // the four waves (through the row-max buffer, free since the last barrier),
+  // then the split's V average (0 for a row with every key of the split masked)
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     float t = l_run[rb] + xor16(l_run[rb]);
-    lsum[rb] = t + xor32(t);
+    t += xor32(t);
+    if (grp == 0) *(LDS_AS float*)(uintptr_t)(rmax_base + ((16 * rb + l16) * NWAVES + wave) * 4) = t;
   }
-  if (grp == 0) {
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-      *(LDS_AS float*)(uintptr_t)(rmax_base + ((16 * rb + l16) * NWAVES + wave) * 4) = lsum[rb];
-  }
+  lds_barrier();
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     if (!row_ok[rb]) continue;
+    const f32x4 wl = *(const LDS_AS f32x4*)(uintptr_t)(rmax_base + (16 * rb + l16) * NWAVES * 4);
+    const float t = (wl[0] + wl[1]) + (wl[2] + wl[3]);
+    const float inv = t > 0.f ? 1.0f / t : 0.f;
     const int64_t rowid = (int64_t)g * a.M + qrow[rb];
-    float* po = a.part_o + rowid * V_DIM + wave * 128 + 4 * grp;
+    uint16_t* po = a.part_o + rowid * V_DIM + wave * 128 + 4 * grp;
 #pragma unroll
-    for (int fb = 0; fb < SM_FB; ++fb) *reinterpret_cast<f32x4*>(po + 16 * fb) = o[fb][rb];
-  }
-  lds_barrier();
-  if (wave == 0 && grp == 0) {
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      if (!row_ok[rb]) continue;
-      const f32x4 wl = *(const LDS_AS f32x4*)(uintptr_t)(rmax_base + (16 * rb + l16) * NWAVES * 4);
-      const float t = (wl[0] + wl[1]) + (wl[2] + wl[3]);
-      const int64_t rowid = (int64_t)g * a.M + qrow[rb];
+    for (int fb = 0; fb < SM_FB; ++fb)
+      *reinterpret_cast<u32x2*>(po + 16 * fb) = u32x2{pack_bf16x2(o[fb][rb][0] * inv, o[fb][rb][1] * inv),
+                                                      pack_bf16x2(o[fb][rb][2] * inv, o[fb][rb][3] * inv)};
+    if (wave == 0 && grp == 0) {
       a.part_ml[2 * rowid] = m_run[rb];
       a.part_ml[2 * rowid + 1] = t;
     }
@@ -1523,6 +1527,8 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
   float l_row = l_run + __shfl_xor(l_run, 16);
   l_row += __shfl_xor(l_row, 32);
   if (row_ok) {
+    // the split's V average (0 for a row with every key of the split masked)
+    const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
     const int64_t rowid = (int64_t)g * a.M + qrow;
     float* po = a.part_o + rowid * V_DIM + 4 * grp;
 #pragma unroll
@@ -1530,7 +1536,7 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)  // feature 64 J + 16 grp + 4 j
         *reinterpret_cast<f32x4*>(po + 64 * J + 12 * grp + 4 * j) =
-            f32x4{o[4 * J][j], o[4 * J + 1][j], o[4 * J + 2][j], o[4 * J + 3][j]};
+            f32x4{o[4 * J][j], o[4 * J + 1][j], o[4 * J + 2][j], o[4 * J + 3][j]} * inv;
     if (grp == 0) {
       a.part_ml[2 * rowid] = m_run;
       a.part_ml[2 * rowid + 1] = l_row;
@@ -1539,15 +1545,19 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
 }
 
 // ------------------------------------------------------------ combine kernel
-// Output row (b, r) = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
-// sequence's splits s, M = max_s m_s, rounded to bf16 (nearest even).
+// Output row (b, r) = sum_s 2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s over
+// the sequence's splits s (o_s the split's V average, l_s its running sum,
+// m_s its running maximum), M = max_s m_s, rounded to bf16 (nearest even).
 // WPR waves share one row: wave k reduces splits k, k + WPR, ... in order, and
 // the WPR wave results are merged in wave order through LDS, so the result
-// does not depend on timing. Lane j covers features 4j .. 4j+3 and
-// 256 + 4j .. +3, so each load instruction reads 1 KB of one partial row. A
-// wave takes its splits COMBINE_BATCH at a time with every load of the batch
-// issued before the first use (one memory round trip per batch), keeping a
-// running maximum and rescaling its sums when the maximum rises.
+// does not depend on timing. A wave takes its splits COMBINE_BATCH at a time
+// with every load of the batch issued before the first use (one memory round
+// trip per batch), keeping a running maximum and rescaling its sums when the
+// maximum rises. The V averages o_s are bf16 on the bf16 path (lane j covers
+// features 8j .. 8j+7: one 16-byte load per partial row and lane) and fp32 on
+// the fp32-input path (F32_OUT; lane j covers 4j .. 4j+3 and 256 + 4j .. +3).
+// HALF: two workgroups per row group, one per half of the 512 features (lane
+// j then covers 4j .. 4j+3 of its half).
 template <int WPR, bool F32_OUT, bool HALF = false>
 __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_kernel(CombineArgs a) {
   constexpr int WAVES = WPR < 4 ? 4 : WPR;
@@ -1559,9 +1569,10 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int sub = wave % WPR;
-  // HALF: two workgroups per row group, one per half of the 512 features.
   const int64_t grow = (int64_t)(HALF ? blockIdx.x >> 1 : blockIdx.x) * ROWS + wave / WPR;
-  const int foff = (HALF ? (blockIdx.x & 1) * 256 : 0) + 4 * lane;  // first feature of this lane
+  // first feature of this lane (acc0); acc1 holds the next four (bf16
+  // partials) or the four 256 further on (fp32 partials)
+  const int foff = HALF ? (blockIdx.x & 1) * 256 + 4 * lane : (F32_OUT ? 4 * lane : 8 * lane);
   const bool active = grow < (int64_t)a.B * a.M;
   const int b = active ? (int)(grow / a.M) : 0;
   const int row = active ? (int)(grow - (int64_t)b * a.M) : 0;
@@ -1590,9 +1601,18 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
         const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * rowid);
         m[j] = ml[0];
         l[j] = ml[1];
-        const float* src = a.part_o + rowid * V_DIM + foff;
-        o0[j] = *reinterpret_cast<const f32x4*>(src);
-        if (!HALF) o1[j] = *reinterpret_cast<const f32x4*>(src + 256);
+        if constexpr (F32_OUT) {
+          const float* src = static_cast<const float*>(a.part_o) + rowid * V_DIM + foff;
+          o0[j] = *reinterpret_cast<const f32x4*>(src);
+          if (!HALF) o1[j] = *reinterpret_cast<const f32x4*>(src + 256);
+        } else if constexpr (HALF) {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.part_o) + rowid * V_DIM + foff);
+          o0[j] = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+        } else {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.part_o) + rowid * V_DIM + foff);
+          o0[j] = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+          o1[j] = f32x4{bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3])};
+        }
       }
     }
     float mb = mloc;
@@ -1607,10 +1627,10 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
     }
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
-      const float w = (m[j] != -INFINITY) ? exp2f(m[j] - mloc) : 0.f;
+      const float w = (m[j] != -INFINITY) ? exp2f(m[j] - mloc) * l[j] : 0.f;
       acc0 += w * o0[j];
       acc1 += w * o1[j];
-      L += w * l[j];
+      L += w;
     }
   }
 
@@ -1638,21 +1658,20 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
   }
   if (!active) return;
   const float inv = L > 0.f ? 1.0f / L : 0.f;
+  acc0 *= inv;
+  acc1 *= inv;
   if constexpr (F32_OUT) {
     float* dst = a.out_f32 + grow * V_DIM + foff;
-    *reinterpret_cast<f32x4*>(dst) = acc0 * inv;
-    if (!HALF) *reinterpret_cast<f32x4*>(dst + 256) = acc1 * inv;
-    return;
+    *reinterpret_cast<f32x4*>(dst) = acc0;
+    if (!HALF) *reinterpret_cast<f32x4*>(dst + 256) = acc1;
+  } else {
+    uint16_t* dst = a.out + grow * V_DIM + foff;
+    const u32x2 p0 = {pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3])};
+    if (HALF)
+      *reinterpret_cast<u32x2*>(dst) = p0;
+    else
+      *reinterpret_cast<u32x4*>(dst) = u32x4{p0[0], p0[1], pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
   }
-  auto pack4 = [&](const f32x4& v) {
-    uint2 p;
-    p.x = (uint32_t)f32_to_bf16_rne(v[0] * inv) | ((uint32_t)f32_to_bf16_rne(v[1] * inv) << 16);
-    p.y = (uint32_t)f32_to_bf16_rne(v[2] * inv) | ((uint32_t)f32_to_bf16_rne(v[3] * inv) << 16);
-    return p;
-  };
-  uint16_t* dst = a.out + grow * V_DIM + foff;
-  *reinterpret_cast<uint2*>(dst) = pack4(acc0);
-  if (!HALF) *reinterpret_cast<uint2*>(dst + 256) = pack4(acc1);
 }
 
 // ------------------------------------------------------------ append kernel
@@ -1805,6 +1824,7 @@ int make_plan(const verify_attn_params* p, Plan* pl, DevShape dv, int rows_per_t
   if (dv.cus < 1 || dv.xcds < 1 || dv.xcds > dv.cus || dv.cus > (1 << 16)) return VERIFY_ATTN_ERR_BAD_DIM;
   const int64_t NUM_CUS = dv.cus;
   const int64_t M = (int64_t)p->num_heads * p->tree_size;
+  const bool bf16_path = rows_per_tile == 0;
   if (rows_per_tile == 0) {
     if (M <= SM_MAX_M) {
       // the rows spread evenly over ceil(M / 32) row tiles
@@ -1880,7 +1900,8 @@ int make_plan(const verify_attn_params* p, Plan* pl, DevShape dv, int rows_per_t
   pl->combine_wpr = wpr;
   pl->combine_halves = halves;
   pl->combine_blocks = (int)cblocks;
-  pl->part_o_bytes = (size_t)max_splits * (size_t)M * V_DIM * sizeof(float);
+  // V averages: bf16 on the bf16 path, fp32 on the fp32-input path
+  pl->part_o_bytes = (size_t)max_splits * (size_t)M * V_DIM * (bf16_path ? 2 : 4);
   pl->ws_bytes = pl->part_o_bytes + (size_t)max_splits * (size_t)M * 2 * sizeof(float);
   return VERIFY_ATTN_OK;
 }
@@ -1913,7 +1934,7 @@ int launch_partial(const verify_attn_params* p, const Plan& pl, const void* q, c
   a.slot_idx = slot_idx;
   a.seq_lens = seq_lens;
   a.tree_parent = tree_parent;
-  a.part_o = static_cast<float*>(workspace);
+  a.part_o = static_cast<uint16_t*>(workspace);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_o_bytes);
   a.B = p->num_seqs;
   a.H = p->num_heads;
@@ -1940,7 +1961,7 @@ int launch_partial(const verify_attn_params* p, const Plan& pl, const void* q, c
 int launch_combine(const verify_attn_params* p, const Plan& pl, const int32_t* seq_lens, void* out,
                    void* workspace, hipStream_t stream, bool f32_out = false) {
   CombineArgs a;
-  a.part_o = static_cast<const float*>(workspace);
+  a.part_o = workspace;
   a.part_ml = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + pl.part_o_bytes);
   a.seq_lens = seq_lens;
   a.out = f32_out ? nullptr : static_cast<uint16_t*>(out);

@@ -57,7 +57,7 @@ def test_workspace_and_plan():
     assert plan["max_splits"] >= -(-65600 // plan["keys_per_split"])
     assert plan["partial_blocks"] % 8 == 0
     assert plan["partial_blocks"] >= plan["max_splits"] * plan["row_tiles"]
-    assert ws == plan["max_splits"] * M * (512 + 2) * 4
+    assert ws == plan["max_splits"] * M * (512 * 2 + 2 * 4)  # bf16 V sums, fp32 (max, sum)
     # nsplit fixes the split length from max_seq_len
     p1 = base_params(nsplit=1)
     assert mtv.verify_attn_plan(p1)["keys_per_split"] >= 65600
@@ -285,6 +285,7 @@ def test_f32_plan_matches_its_workspace():
     p = base_params()
     plan = mtv.verify_attn_plan_for(p, True)
     assert plan["keys_per_tile"] == 16 and plan["rows_per_tile"] == 64
+    # fp32 V sums and (max, sum) pairs
     assert mtv.verify_attn_f32_workspace_size(p) == plan["max_splits"] * 8 * 64 * (512 + 2) * 4
 
 
@@ -312,7 +313,8 @@ def test_plan_covers_every_split():
         assert splits <= plan["max_splits"], (B, H, T, max_len, total, nsplit, plan)
         assert plan["partial_blocks"] >= plan["max_splits"] * plan["row_tiles"]
         assert plan["row_tiles"] * plan["rows_per_tile"] >= H * T
-        assert mtv.verify_attn_workspace_size(p) == plan["max_splits"] * H * T * (512 + 2) * 4
+        # bf16 V sums [max_splits][H*T][512], then fp32 (max, sum) pairs
+        assert mtv.verify_attn_workspace_size(p) == plan["max_splits"] * H * T * (512 * 2 + 2 * 4)
         assert mtv.verify_attn_f32_workspace_size(p) > 0
 
 

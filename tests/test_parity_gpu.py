@@ -250,12 +250,22 @@ def test_zero_query_is_mean(orc):
     check_full(orc, wl)
 
 
-def test_constant_column():
-    wl = small(H=4, T=8, prefixes=[777], seed=9)
-    c = inputs.f32_to_bf16_bits(np.array([0.375], np.float32))[0]
-    wl.kv_pool[:, 100] = c
-    got = run_gpu(wl)
-    assert np.all(got[..., 100] == np.float32(0.375))
+@pytest.mark.parametrize("H,T,prefix,nsplit", [
+    (4, 8, 777, 0),       # small-row kernel
+    (4, 8, 5000, 9),      # small-row kernel, nine splits merged by the combine
+    (8, 16, 3000, 0),     # 128-row kernel
+    (8, 16, 20000, 40),   # 128-row kernel, forty splits
+])
+def test_constant_column(H, T, prefix, nsplit):
+    """Softmax weights sum to one, so a feature that is the same in every KV row
+    comes out as exactly that value, whatever the splits and their merge."""
+    wl = small(H=H, T=T, prefixes=[prefix], seed=9)
+    for f, v in ((100, 0.375), (511, -3.0e-3), (7, 1.5e4)):
+        wl.kv_pool[:, f] = inputs.f32_to_bf16_bits(np.array([v], np.float32))[0]
+    got = run_gpu(wl, nsplit)
+    for f, v in ((100, 0.375), (511, -3.0e-3), (7, 1.5e4)):
+        want = inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(np.array([v], np.float32)))[0]
+        assert np.all(got[..., f] == want), (f, np.unique(got[..., f]))
 
 
 def test_slot_permutation_bitwise():

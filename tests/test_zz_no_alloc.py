@@ -37,7 +37,7 @@ def _both(wl):
 
 def test_noalloc_matches_verify_attn_on_consecutive_calls():
     import torch
-    big = inputs.config("c4a_long_scattered")  # 64.25 MiB of partials, near the scratch's 80 MiB
+    big = inputs.config("c4a_long_scattered")  # 32.25 MiB of partials, the largest one-round plan
     small = inputs.make_workload("small", B=3, H=8, T=9, prefixes=[700, 0, 2048], pool_slots=4096,
                                  seed=77)
     for wl in (big, small):
