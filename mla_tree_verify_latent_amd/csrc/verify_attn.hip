@@ -61,7 +61,11 @@ constexpr float LAZY_RESCALE_LOG2 = 8.0f;  // running max is raised only past +8
 constexpr int QK_AHEAD = 4;                // K operand reads in flight ahead of their MFMA
 constexpr int PV_AHEAD = 4;                // V^T operand reads in flight ahead
 constexpr int SM_PIECES = 16;              // softmax pieces interleaved with the next QK
-constexpr int COMBINE_BATCH = 8;           // partials per batch of loads in the combine kernel
+// partials per batch of loads in the combine kernel: bf16 whole rows, bf16
+// half rows, fp32 (about 100-110 VGPRs each: four waves per SIMD)
+constexpr int COMBINE_BATCH = 12;
+constexpr int COMBINE_BATCH_HALF = 16;
+constexpr int COMBINE_BATCH_F32 = 8;
 constexpr int QSTAGE_PIECES = KV_DIM / 2 / 8;  // 36 16-byte pieces per row and half
 constexpr int QSTAGE_BYTES = ROWS_PER_WAVE * QSTAGE_PIECES * 16;  // 18 KB per wave
 constexpr int QSTAGE_LOADS = QSTAGE_BYTES / 1024;                 // 18 direct-to-LDS loads
@@ -1550,19 +1554,20 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
 // m_s its running maximum), M = max_s m_s, rounded to bf16 (nearest even).
 // WPR waves share one row: wave k reduces splits k, k + WPR, ... in order, and
 // the WPR wave results are merged in wave order through LDS, so the result
-// does not depend on timing. A wave takes its splits COMBINE_BATCH at a time
-// with every load of the batch issued before the first use (one memory round
-// trip per batch), keeping a running maximum and rescaling its sums when the
-// maximum rises. The V averages o_s are bf16 on the bf16 path (lane j covers
-// features 8j .. 8j+7: one 16-byte load per partial row and lane) and fp32 on
-// the fp32-input path (F32_OUT; lane j covers 4j .. 4j+3 and 256 + 4j .. +3).
+// does not depend on timing. A wave takes its splits a batch at a time
+// (COMBINE_BATCH, _HALF or _F32 of them) with every load of the
+// batch issued before the first use (one memory round trip per batch),
+// keeping a running maximum and rescaling its sums when the maximum rises.
+// The V averages o_s are bf16 on the bf16 path (lane j covers features
+// 8j .. 8j+7: one 16-byte load per partial row and lane) and fp32 on the
+// fp32-input path (F32_OUT; lane j covers 4j .. 4j+3 and 256 + 4j .. +3).
 // HALF: two workgroups per row group, one per half of the 512 features (lane
 // j then covers 4j .. 4j+3 of its half).
 template <int WPR, bool F32_OUT, bool HALF = false>
 __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_kernel(CombineArgs a) {
   constexpr int WAVES = WPR < 4 ? 4 : WPR;
   constexpr int ROWS = WAVES / WPR;
-  constexpr int BATCH = COMBINE_BATCH;
+  constexpr int BATCH = F32_OUT ? COMBINE_BATCH_F32 : (HALF ? COMBINE_BATCH_HALF : COMBINE_BATCH);
   __shared__ float red_ml[WAVES][2];
   __shared__ f32x4 red_o[WPR > 1 ? WAVES : 1][2 * 64];
 
@@ -1577,47 +1582,59 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
   const int b = active ? (int)(grow / a.M) : 0;
   const int row = active ? (int)(grow - (int64_t)b * a.M) : 0;
 
-  SplitLoc loc;
-  loc.g0 = 0;
-  loc.n_splits = 0;
-  if (active && !locate_split(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, b, true, &loc)) loc.n_splits = 0;
-  int g_end = loc.g0 + loc.n_splits;
+  // One batch: partials base + j * WPR (j < BATCH) below `limit`, as loaded
+  // (ra: the V average's bits at foff; rb: fp32 at foff + 256). Entries at or
+  // past the limit are left unloaded and never read.
+  f32x2 ml[BATCH];
+  u32x4 ra[BATCH];
+  u32x4 rb[F32_OUT && !HALF ? BATCH : 1];
+  auto load = [&](int base, int limit) {
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      if (base + j * WPR >= limit) continue;  // wave-uniform
+      const int64_t rowid = (int64_t)(base + j * WPR) * a.M + row;
+      ml[j] = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * rowid);
+      if constexpr (F32_OUT) {
+        const float* src = static_cast<const float*>(a.part_o) + rowid * V_DIM + foff;
+        ra[j] = *reinterpret_cast<const u32x4*>(src);
+        if constexpr (!HALF) rb[j] = *reinterpret_cast<const u32x4*>(src + 256);
+      } else if constexpr (HALF) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.part_o) + rowid * V_DIM + foff);
+        ra[j] = u32x4{w[0], w[1], 0u, 0u};
+      } else {
+        ra[j] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.part_o) + rowid * V_DIM + foff);
+      }
+    }
+  };
+
+  // Sequence 0's splits start at global split 0, so its rows issue their first
+  // batch (bounded by max_splits, inside the workspace) before the split count
+  // is known; every other row locates its sequence's splits first.
+  const bool first_seq = active && b == 0;
+  int g0 = 0, g_end = 0;
+  if (first_seq) {
+    load(sub, a.max_splits);
+    const int len = clamp_len(a.seq_lens[0], a.T, a.max_seq_len);
+    g_end = (len + a.chunk - 1) / a.chunk;
+  } else if (active) {
+    SplitLoc loc;
+    if (locate_split(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, b, true, &loc)) {
+      g0 = loc.g0;
+      g_end = loc.g0 + loc.n_splits;
+    }
+  }
   g_end = g_end < a.max_splits ? g_end : a.max_splits;
+  int base = g0 + sub;
+  if (!first_seq && base < g_end) load(base, g_end);
 
   float mloc = -INFINITY;  // running maximum of this wave's splits
   float L = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int base = loc.g0 + sub; base < g_end; base += WPR * BATCH) {
-    float m[BATCH], l[BATCH];
-    f32x4 o0[BATCH], o1[BATCH];
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      m[j] = -INFINITY;
-      l[j] = 0.f;
-      o0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      o1[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (base + j * WPR < g_end) {  // wave-uniform
-        const int64_t rowid = (int64_t)(base + j * WPR) * a.M + row;
-        const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * rowid);
-        m[j] = ml[0];
-        l[j] = ml[1];
-        if constexpr (F32_OUT) {
-          const float* src = static_cast<const float*>(a.part_o) + rowid * V_DIM + foff;
-          o0[j] = *reinterpret_cast<const f32x4*>(src);
-          if (!HALF) o1[j] = *reinterpret_cast<const f32x4*>(src + 256);
-        } else if constexpr (HALF) {
-          const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.part_o) + rowid * V_DIM + foff);
-          o0[j] = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
-        } else {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.part_o) + rowid * V_DIM + foff);
-          o0[j] = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
-          o1[j] = f32x4{bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3])};
-        }
-      }
-    }
+  while (base < g_end) {
     float mb = mloc;
 #pragma unroll
-    for (int j = 0; j < BATCH; ++j) mb = fmaxf(mb, m[j]);
+    for (int j = 0; j < BATCH; ++j)
+      if (base + j * WPR < g_end) mb = fmaxf(mb, ml[j][0]);
     if (mb > mloc) {  // the same for every lane (one row per wave)
       const float s = exp2f(mloc - mb);  // mloc = -inf -> 0
       acc0 *= s;
@@ -1627,11 +1644,23 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
     }
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
-      const float w = (m[j] != -INFINITY) ? exp2f(m[j] - mloc) * l[j] : 0.f;
-      acc0 += w * o0[j];
-      acc1 += w * o1[j];
+      if (base + j * WPR >= g_end || ml[j][0] == -INFINITY) continue;  // wave-uniform
+      const float w = exp2f(ml[j][0] - mloc) * ml[j][1];
+      f32x4 o0, o1;
+      if constexpr (F32_OUT) {
+        o0 = __builtin_bit_cast(f32x4, ra[j]);
+        o1 = HALF ? f32x4{0.f, 0.f, 0.f, 0.f} : __builtin_bit_cast(f32x4, rb[HALF ? 0 : j]);
+      } else {
+        o0 = f32x4{bf16_lo(ra[j][0]), bf16_hi(ra[j][0]), bf16_lo(ra[j][1]), bf16_hi(ra[j][1])};
+        o1 = HALF ? f32x4{0.f, 0.f, 0.f, 0.f}
+                  : f32x4{bf16_lo(ra[j][2]), bf16_hi(ra[j][2]), bf16_lo(ra[j][3]), bf16_hi(ra[j][3])};
+      }
+      acc0 += w * o0;
+      acc1 += w * o1;
       L += w;
     }
+    base += WPR * BATCH;
+    if (base < g_end) load(base, g_end);
   }
 
   if constexpr (WPR > 1) {

@@ -244,6 +244,26 @@ def test_nsplit_independent(orc, nsplit):
     check_full(orc, wl, nsplit=nsplit)
 
 
+@pytest.mark.parametrize("case", [
+    dict(B=1, H=64, T=64, prefixes=[6000], nsplit=40),           # 4096 rows, one wave per row
+    dict(B=3, H=64, T=16, prefixes=[3000, 0, 5000], nsplit=48),  # rows of sequences 1 and 2 locate their splits
+    dict(B=1, H=8, T=1, prefixes=[60000], nsplit=600),           # 8 rows: half rows, 16 waves per row
+    dict(B=2, H=8, T=2, prefixes=[30000, 20000], nsplit=800),
+], ids=lambda c: "B{B}_H{H}_T{T}_n{nsplit}".format(**c))
+def test_combine_batches(orc, case):
+    """Splits enough that every combine wave takes several batches of loads
+    (at most 16 partials per batch, at most 16 waves per row)."""
+    import mla_tree_verify_latent_amd as mtv
+    case = dict(case)
+    nsplit = case.pop("nsplit")
+    wl = small("combine", pool=sum(case["prefixes"]) + case["B"] * case["T"] + 300, seed=21, **case)
+    plan = mtv.verify_attn_plan(params_of(wl, nsplit))
+    c = plan["keys_per_split"]
+    per_seq = [-(-(p + wl.T) // c) for p in case["prefixes"]]
+    assert max(per_seq) > 16 * 16 or (wl.H * wl.T * case["B"] > 2048 and max(per_seq) > 12), per_seq
+    check_full(orc, wl, nsplit=nsplit)
+
+
 def test_zero_query_is_mean(orc):
     wl = small(H=2, T=12, prefixes=[500], seed=8)
     wl.q[:] = 0
