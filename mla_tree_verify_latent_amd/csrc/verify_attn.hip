@@ -1797,7 +1797,6 @@ __global__ __launch_bounds__(256) void verify_attn_validate_kernel(ValidateArgs 
 
 constexpr int MI355X_CUS = 256;     // compute units of a whole MI355X (the plan's default)
 constexpr int MI355X_XCDS = 8;      // and its XCDs
-constexpr int MIN_CHUNK = 256;      // keys per split below which partials dominate
 constexpr int64_t COMBINE_WAVES_PER_CU = 16;  // combine waves resident at once per CU
 constexpr int64_t ROUND_COST_TILES = 4;  // fixed cost of a round of workgroups, in tiles
 
@@ -1870,7 +1869,7 @@ int make_plan(const verify_attn_params* p, Plan* pl, DevShape dv, int rows_per_t
     chunk = ceil_div64(p->max_seq_len, p->nsplit);
   } else {
     // For R = 1, 2, ... rounds of one workgroup per CU, take the shortest split
-    // (a multiple of nk, at least MIN_CHUNK) whose item count fits R rounds
+    // (a multiple of nk, at least one tile) whose item count fits R rounds
     // whatever the lengths are: with total_kv keys over num_seqs sequences there
     // are at most ceil(total_kv / c) + num_seqs - 1 splits. Keep the split with
     // the lowest estimated time, in units of one tile of nk keys: every round
@@ -1879,7 +1878,7 @@ int make_plan(const verify_attn_params* p, Plan* pl, DevShape dv, int rows_per_t
     // tile of partial traffic (written, then read by the combine). More, shorter
     // splits fill the last round better but add fixed costs and partials.
     const int64_t split_cap = ceil_div64(p->max_seq_len, nk) * nk;  // one split per sequence
-    const int64_t floor_c = ceil_div64(MIN_CHUNK, nk) * nk;
+    const int64_t floor_c = nk;
     // fewest rounds with room for every sequence's last split
     const int64_t r0 = ceil_div64((int64_t)p->num_seqs * row_tiles, NUM_CUS);
     int64_t best = 0, best_cost = INT64_MAX;
@@ -1887,7 +1886,7 @@ int make_plan(const verify_attn_params* p, Plan* pl, DevShape dv, int rows_per_t
       const int64_t splits = NUM_CUS * R / row_tiles - (p->num_seqs - 1);
       if (splits < 1) continue;
       int64_t c = ceil_div64(p->total_kv, splits);
-      c = ceil_div64(c < MIN_CHUNK ? MIN_CHUNK : c, nk) * nk;
+      c = ceil_div64(c, nk) * nk;
       if (c > split_cap) c = split_cap;
       const int64_t items = (ceil_div64(p->total_kv, c) + p->num_seqs - 1) * row_tiles;
       const int64_t cost = ceil_div64(items, NUM_CUS) * (20 * (c / nk) + 20 * ROUND_COST_TILES) + items;

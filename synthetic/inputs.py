@@ -137,8 +137,11 @@ def make_workload(
     ``tree``: "random" (uniform parents, optional depth cap), "chain" or "flat".
     ``layout``: "scattered" (page_size=1, one seeded permutation of all pool
     slots, sequences take consecutive slices of it: prefix rows then tree rows),
-    or "contiguous" (the same row values moved so that the slot list of all
-    sequences is 0, 1, 2, ...; page_size=64).
+    "contiguous" (the same row values moved so that the slot list of all
+    sequences is 0, 1, 2, ...; page_size=64), or "paged64" (the same row values
+    moved so that every run of 64 consecutive slot-list entries fills one page
+    of 64 consecutive slots, the pages in seeded random order over the pool;
+    page_size=64).
     ``dtype``: "bf16" (values rounded to nearest even, stored as bit patterns)
     or "f32" (the same draws kept as binary32 values).
     """
@@ -185,6 +188,23 @@ def make_workload(
         kv_pool = np.ascontiguousarray(kv_pool[order])
         slot_idx = np.arange(total, dtype=np.int32)
         page_size = 64
+    elif layout == "paged64":
+        # Logical row i of the slot list goes to slot 64 * page[i // 64] + i % 64.
+        n_pages = pool_slots // 64
+        assert -(-total // 64) <= n_pages, "pool too small for 64-row pages"
+        page = np.random.Generator(np.random.PCG64(seed + 1)).permutation(n_pages)
+        i = np.arange(total, dtype=np.int64)
+        new_slot = 64 * page[i // 64] + i % 64
+        moved = np.zeros(pool_slots, dtype=bool)
+        moved[new_slot] = True
+        rest_slots = np.flatnonzero(~moved)
+        rest_rows = perm[total:][:rest_slots.size]
+        pool = np.empty_like(kv_pool)
+        pool[new_slot] = kv_pool[slot_idx]
+        pool[rest_slots] = kv_pool[rest_rows]
+        kv_pool = pool
+        slot_idx = new_slot.astype(np.int32)
+        page_size = 64
     elif layout != "scattered":
         raise ValueError(layout)
 
@@ -198,7 +218,8 @@ def make_workload(
 
 # The named workloads: the five configurations the benchmark is specified on
 # (tiny smoke case, TP-share decode verify, full-head verify, long-context
-# verify in two layouts, ragged batch) plus two extra points at 65k context.
+# verify in two layouts, ragged batch) plus two extra points at 65k context
+# (the production H=8, T=9 shape also in two more layouts).
 CONFIGS = {
     "c1_tiny": dict(B=1, H=8, T=8, prefixes=[256], pool_slots=1024, seed=1000),
     "c2_tp_share": dict(B=1, H=8, T=32, prefixes=[4096], pool_slots=65536, seed=2000, max_depth=8),
@@ -210,6 +231,11 @@ CONFIGS = {
                       seed=5000),
     "e1_h64_65k": dict(B=1, H=64, T=64, prefixes=[65536], pool_slots=131072, seed=6000),
     "e2_h8_t9_65k": dict(B=1, H=8, T=9, prefixes=[65536], pool_slots=131072, seed=7000),
+    # the same production shape with its KV rows defragmented, and in 64-row pages
+    "e2_h8_t9_65k_contiguous": dict(B=1, H=8, T=9, prefixes=[65536], pool_slots=131072, seed=7000,
+                                    layout="contiguous"),
+    "e2_h8_t9_65k_paged64": dict(B=1, H=8, T=9, prefixes=[65536], pool_slots=131072, seed=7000,
+                                 layout="paged64"),
     # fp32 inputs (binary32 q and KV pool) at the 64k-token H=8 shape
     "f4_long_f32": dict(B=1, H=8, T=64, prefixes=[65536], pool_slots=131072, seed=4000,
                         dtype="f32"),

@@ -46,6 +46,27 @@ def test_oracle_verify_is_layout_independent():
     assert np.array_equal(orc.run(scat), orc.run(cont))
 
 
+def test_paged64_layout_holds_the_same_rows():
+    """The 64-row paged layout: logical row i of the slot list holds the row it
+    holds in the scattered layout of the same seed, every run of 64 entries is
+    one page of 64 consecutive slots starting at a multiple of 64, the pool is a
+    permutation of the scattered pool's rows, and the oracle's result is the
+    same in every layout."""
+    small = dict(B=3, H=2, T=5, prefixes=[130, 0, 333], pool_slots=1024)
+    scat = inputs.make_workload("paged", seed=43, **small)
+    paged = inputs.make_workload("paged", seed=43, layout="paged64", **small)
+    assert np.array_equal(paged.kv_pool[paged.slot_idx], scat.kv_pool[scat.slot_idx])
+    s = paged.slot_idx.astype(np.int64)
+    i = np.arange(s.size)
+    assert np.all(s % 64 == i % 64)
+    assert np.all(s - i % 64 == np.repeat(s[::64], 64)[:s.size])
+    assert len(np.unique(s[::64])) == len(s[::64])
+    key = lambda pool: sorted(r.tobytes() for r in pool)
+    assert key(paged.kv_pool) == key(scat.kv_pool)
+    orc = oracle.load()
+    assert np.array_equal(orc.run(paged), orc.run(scat))
+
+
 def _bf16_dev(a):
     import torch
     return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
@@ -152,3 +173,20 @@ def test_compact_then_verify_in_one_graph():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("shape", ["small", "e2_h8_t9_65k"])
+def test_layouts_give_identical_output(shape):
+    """Verify reads KV rows only through the slot list: scattered, contiguous
+    and 64-row paged layouts of the same rows give the same bits."""
+    from helpers import run_gpu
+    outs = []
+    for layout in ("scattered", "contiguous", "paged64"):
+        if shape == "small":
+            wl = inputs.make_workload("layouts", B=2, H=8, T=9, prefixes=[3000, 1000], pool_slots=8192,
+                                      seed=44, layout=layout)
+        else:
+            wl = inputs.make_workload(shape, **{**inputs.CONFIGS[shape], "layout": layout})
+        outs.append(run_gpu(wl))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])

@@ -36,6 +36,13 @@ def orc():
     return oracle.load()
 
 
+# The synthetic shapes hold a few thousand keys per sequence, where the
+# library's own plan takes splits of one or two tiles: too short for a running
+# maximum to rise within a split. Four splits per sequence make them hundreds
+# of keys (several tiles) long.
+FORCED_SPLITS = {"small": 4, "ragged": 4, "few_rows": 4, "decode": 4}
+
+
 def _plan(wl, nsplit=0):
     import mla_tree_verify_latent_amd as mtv
     return mtv.verify_attn_plan_for(params_of(wl, nsplit), wl.f32)
@@ -85,8 +92,9 @@ def test_peaked_queries(orc, shape, q_std):
     if shape == "decode" and q_std == 16:
         q_std = 32  # 8 query rows at spread 16 never overtake a running maximum by 8
     wl = _workload(shape, seed=50 + q_std, q_std=float(q_std))
-    _show_rescale(wl)
-    _check_bf16(orc, wl)
+    nsplit = FORCED_SPLITS.get(shape, 0)
+    _show_rescale(wl, nsplit)
+    _check_bf16(orc, wl, nsplit)
 
 
 @pytest.mark.parametrize("shape,amp,period,offset,nsplit", [
@@ -96,12 +104,13 @@ def test_peaked_queries(orc, shape, q_std):
     ("ragged", 60.0, 333, 5, 0),
     ("e2_h8_t9_65k", 40.0, None, 0, 0),
     ("c4a_long_scattered", 80.0, None, 0, 0),
-    ("few_rows", 60.0, None, 0, 0),        # 32 rows: the small-row kernel, one split per ramp
+    ("few_rows", 60.0, None, 0, 0),        # 32 rows: the small-row kernel, one ramp per split
     ("few_rows", 300.0, 700, 123, 0),
     ("decode", 200.0, None, 0, 1),         # T = 1, one split of each whole sequence
 ], ids=lambda v: str(v))
 def test_score_ramp(orc, shape, amp, period, offset, nsplit):
     wl = _workload(shape, seed=70)
+    nsplit = nsplit or FORCED_SPLITS.get(shape, 0)
     if period is None:  # aligned with the splits, or the whole sequence for one split
         period = _plan(wl, nsplit)["keys_per_split"] if nsplit != 1 else int(wl.seq_lens.max())
     rescale.plant_score_ramp(wl, amp, period, offset)
@@ -117,8 +126,9 @@ def test_score_ramp(orc, shape, amp, period, offset, nsplit):
 @pytest.mark.parametrize("shape", ["small", "ragged"])
 def test_peaked_queries_f32(orc, shape, q_std):
     wl = _workload(shape, seed=90 + q_std, dtype="f32", q_std=float(q_std))
-    _show_rescale(wl)
-    _check_f32(orc, wl)
+    nsplit = FORCED_SPLITS.get(shape, 0)
+    _show_rescale(wl, nsplit)
+    _check_f32(orc, wl, nsplit)
 
 
 @pytest.mark.parametrize("shape,amp,period,offset,nsplit", [
@@ -129,6 +139,7 @@ def test_peaked_queries_f32(orc, shape, q_std):
 ], ids=lambda v: str(v))
 def test_score_ramp_f32(orc, shape, amp, period, offset, nsplit):
     wl = _workload(shape, seed=110, dtype="f32")
+    nsplit = nsplit or FORCED_SPLITS.get(shape, 0)
     if period is None:
         period = _plan(wl, nsplit)["keys_per_split"] if nsplit != 1 else int(wl.seq_lens.max())
     rescale.plant_score_ramp(wl, amp, period, offset)
