@@ -62,22 +62,35 @@ def check_registers(extra=()) -> dict:
             raise RuntimeError(f"{kname} register allocation changed: {p}")
     check_mfma_hazards(text, "verify_attn_f32_partial_kernel")
     for kernel in ("verify_attn_partial_small_kernelILi1E", "verify_attn_partial_small_kernelILi2E"):
+        check_mfma_hazards(text, kernel)
+        check_asm_b_operands_invariant(text, kernel)
         check_asm_mfma_result_reads(text, kernel)
     return info
 
 
-def _vregs(tok):
-    m = re.match(r"v\[(\d+):(\d+)\]$", tok)
+def _regs(tok, kind="v"):
+    """Register numbers of one operand token of register file `kind` ("v" or "a")."""
+    tok = tok.split()[0] if tok.split() else tok  # drop modifiers such as "offset:16"
+    m = re.match(kind + r"\[(\d+):(\d+)\]$", tok)
     if m:
         return set(range(int(m.group(1)), int(m.group(2)) + 1))
-    m = re.match(r"v(\d+)$", tok)
+    m = re.match(kind + r"(\d+)$", tok)
     return {int(m.group(1))} if m else set()
 
 
+def _vregs(tok):
+    return _regs(tok, "v")
+
+
+def _operands(line):
+    return [t.strip() for t in line.split(None, 1)[1].split(",")] if " " in line else []
+
+
 def check_mfma_hazards(text, kernel):
-    """The asm MFMAs of `kernel` that accumulate in AGPRs carry no wait states
-    of their own: require that none of the two instructions issued before one
-    of them is a VALU instruction writing one of its source VGPRs."""
+    """The asm MFMAs of `kernel` with an AGPR operand carry no wait states of
+    their own: require that none of the two instructions issued before one of
+    them is a VALU instruction writing one of its source registers (VGPR or
+    AGPR)."""
     # the kernel's entry label: a line "<mangled name containing `kernel`>:"
     m = re.search(r"^(_Z\S*" + re.escape(kernel) + r"\S*):", text, flags=re.M)
     if not m:
@@ -89,8 +102,8 @@ def check_mfma_hazards(text, kernel):
     for i, line in enumerate(ins):
         if not (line.startswith("v_mfma") and " a[" in line):
             continue
-        ops = [t.strip() for t in line.split(None, 1)[1].split(",")]
-        src = _vregs(ops[1]) | _vregs(ops[2])
+        ops = _operands(line)
+        src = {("v", r) for t in ops[1:] for r in _regs(t, "v")} | {("a", r) for t in ops[1:] for r in _regs(t, "a")}
         issued, k = 0, i - 1
         while k >= 0 and issued < 2:
             prev = ins[k]
@@ -102,7 +115,8 @@ def check_mfma_hazards(text, kernel):
                 continue
             issued += 1
             if prev.startswith("v_") and not prev.startswith("v_mfma"):
-                dst = _vregs(prev.split(None, 1)[1].split(",")[0].strip())
+                d = _operands(prev)[0]
+                dst = {("v", r) for r in _regs(d, "v")} | {("a", r) for r in _regs(d, "a")}
                 if dst & src:
                     raise RuntimeError(f"{kernel}: VALU write right before an asm MFMA source: "
                                        f"{prev!r} -> {line!r}")
@@ -118,20 +132,45 @@ def _kernel_body(text, kernel):
     return [l for l in ins if l and not l.startswith(".") and not l.endswith(":")]
 
 
+def check_asm_b_operands_invariant(text, kernel):
+    """The QK MFMAs of the small-row kernel read the query from AGPRs (their B
+    operand) for the whole split: require that no instruction between
+    the first and the last of them writes one of those AGPRs (a copy into an
+    AGPR right before an asm MFMA would need wait states the compiler does not
+    know to insert)."""
+    ins = _kernel_body(text, kernel)
+    mf = [i for i, l in enumerate(ins) if l.startswith("v_mfma") and ", a[" in l]
+    if not mf:
+        raise RuntimeError(f"{kernel}: no asm MFMA with an AGPR operand found")
+    b_regs = set()
+    for i in mf:
+        b_regs |= _regs(_operands(ins[i])[2], "a")
+    for line in ins[mf[0]:mf[-1]]:
+        if line.startswith("v_mfma") or not _operands(line):
+            continue
+        if line.startswith(("s_", "ds_write", "global_store", "buffer_store")):
+            continue  # no AGPR destination
+        if _regs(_operands(line)[0], "a") & b_regs:
+            raise RuntimeError(f"{kernel}: {line!r} writes a query AGPR between the QK MFMAs")
+
+
 def check_asm_mfma_result_reads(text, kernel):
     """The QK MFMAs of the small-row kernel are asm statements (B operand in
-    AGPRs) whose VGPR results the compiler does not know to be late: require
-    that no VALU instruction reads one of their results before the next drain
-    (an 's_nop 7') or the next MFMA."""
+    AGPRs) whose VGPR results the compiler does not know to be late:
+    require that no VALU or LDS-write instruction reads one of their results
+    before the next drain (an 's_nop 7'). Later MFMAs may read it (as their
+    accumulator: the matrix unit orders that itself)."""
     ins = _kernel_body(text, kernel)
     for i, line in enumerate(ins):
         if not (line.startswith("v_mfma") and ", a[" in line):
             continue
         dst = _vregs(line.split(None, 1)[1].split(",")[0].strip())
-        for later in ins[i + 1:i + 60]:
-            if later.startswith("s_nop 7") or later.startswith("v_mfma"):
+        for later in ins[i + 1:i + 400]:
+            if later.startswith("s_nop 7"):
                 break
-            if later.startswith("v_") and "," in later:
+            if later.startswith("v_mfma"):
+                continue
+            if (later.startswith("v_") or later.startswith("ds_write")) and "," in later:
                 srcs = set()
                 for tok in later.split(None, 1)[1].split(",")[1:]:
                     srcs |= _vregs(tok.strip())

@@ -358,3 +358,16 @@ def test_binding_refuses_tensors_on_another_device():
         _check_device(s0, t(d0), t(d1))
     with pytest.raises(ValueError, match="would run on"):
         _check_device(s0, t(d1), t(d1))
+
+
+def test_plan_row_kernel_bands():
+    """Rows per sequence pick the kernel: at most 32 the small-row kernel (64-key
+    tiles, one row tile), more the 128-row kernel (32-key tiles)."""
+    for H, T in [(1, 1), (8, 1), (8, 4), (4, 8), (16, 2), (3, 11), (8, 5), (8, 9), (16, 5), (8, 10),
+                 (1, 64), (81, 1), (8, 11), (16, 8), (64, 64)]:
+        M = H * T
+        plan = mtv.verify_attn_plan(base_params(num_heads=H, tree_size=T))
+        if M <= 32:
+            assert plan["keys_per_tile"] == 64 and plan["row_tiles"] == 1 and plan["rows_per_tile"] == M, (H, T, plan)
+        else:
+            assert plan["keys_per_tile"] == 32 and plan["rows_per_tile"] == 128, (H, T, plan)
