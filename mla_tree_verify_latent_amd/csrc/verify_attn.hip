@@ -218,6 +218,19 @@ __device__ int count_splits(const int32_t* __restrict__ seq_lens, int B, int T, 
 // split then share that XCD's L2 for their KV reads). For B <= 64 one load of
 // seq_lens serves both the item count and the split's location; larger
 // batches scan twice.
+// seq_lens[0] through the scalar cache (a uniform value: one load per wave on
+// the scalar path, which the first vector loads of every workgroup do not
+// queue behind). The wait is part of the statement, so the value is in its
+// register when the statement ends.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ int load_first_len(const int32_t* seq_lens) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(seq_lens) : "memory");
+  return v;
+}
+#pragma clang diagnostic pop
+
 __device__ bool locate_item(const int32_t* __restrict__ seq_lens, int B, int T, int max_len, int chunk,
                             int max_splits, int row_tiles, int nxcd, int* g_out, int* rt_out, SplitLoc* loc) {
   const int lane = threadIdx.x & 63;
@@ -231,6 +244,24 @@ __device__ bool locate_item(const int32_t* __restrict__ seq_lens, int B, int T, 
     *g_out = logical / row_tiles;
     *rt_out = logical - *g_out * row_tiles;
     return locate_split(seq_lens, B, T, max_len, chunk, *g_out, false, loc);
+  }
+  if (B == 1) {  // one sequence: its length is one uniform (scalar) load, no scan
+    const int len = clamp_len(load_first_len(seq_lens), T, max_len);
+    const int ns = (len + chunk - 1) / chunk;
+    const int n_items = min(ns, max_splits) * row_tiles;
+    const int per_xcd = (n_items + nxcd - 1) / nxcd;
+    const int k_on_xcd = blockIdx.x / nxcd;
+    const int logical = (blockIdx.x - k_on_xcd * nxcd) * per_xcd + k_on_xcd;
+    if (k_on_xcd >= per_xcd || logical >= n_items) return false;
+    const int g = logical / row_tiles;
+    loc->b = 0;
+    loc->g0 = 0;
+    loc->n_splits = ns;
+    loc->len = len;
+    loc->seg = 0;
+    *g_out = g;
+    *rt_out = logical - g * row_tiles;
+    return true;
   }
   int len = 0, ns = 0;
   if (lane < B) {
