@@ -183,6 +183,35 @@ def test_length_bound_above_actual(orc, extra):
     assert ok, f"worst row {idx} at {worst:.2f} bf16 ulp"
 
 
+@pytest.mark.parametrize("H,T,prefix", [(8, 16, 2072), (8, 4, 2072), (4, 3, 1000)])
+@pytest.mark.parametrize("extra", [40, 3000])
+def test_rows_past_the_end_are_never_read(orc, H, T, prefix, extra):
+    """One sequence whose slot table and length bound run `extra` entries past
+    its length, every one of them naming a pool row of bf16 NaNs: a split that
+    starts before the end reads no KV row past it (its last tiles are masked,
+    and a masked NaN row would still turn the weighted V sum into NaN), and the
+    splits dealt past the end do nothing. Covers the 128-row kernel and the
+    small-row kernel with one and two 16-row blocks; the output passes the
+    oracle gate of the unextended inputs."""
+    import torch
+    import mla_tree_verify_latent_amd as mtv
+    wl = small(B=1, H=H, T=T, prefixes=[prefix], seed=37)
+    dev = to_device(wl)
+    nan_rows = torch.full((extra, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dev["kv_pool"] = torch.cat([dev["kv_pool"], nan_rows])
+    past = torch.arange(wl.pool_slots, wl.pool_slots + extra, dtype=torch.int32, device="cuda")
+    dev["slot_idx"] = torch.cat([dev["slot_idx"], past])
+    prm = mtv.make_params(num_seqs=1, num_heads=H, tree_size=T, max_seq_len=wl.max_seq_len + extra,
+                          total_kv=wl.total_kv + extra, pool_slots=wl.pool_slots + extra,
+                          sm_scale=wl.sm_scale)
+    out = mtv.VerifyAttention(prm)(**dev)
+    torch.cuda.synchronize()
+    got = bf16_out_to_f32(out)
+    assert np.isfinite(got).all()
+    ok, worst, idx = parity_gate(got, orc.run(wl))
+    assert ok, f"worst row {idx} at {worst:.2f} bf16 ulp"
+
+
 @pytest.mark.parametrize("tree", ["flat", "chain"])
 def test_tree_shapes(orc, tree):
     check_full(orc, small(H=4, T=64, prefixes=[300], tree=tree, seed=5))
