@@ -66,6 +66,8 @@ constexpr int SM_PIECES = 16;              // softmax pieces interleaved with th
 constexpr int COMBINE_BATCH = 12;
 constexpr int COMBINE_BATCH_HALF = 16;
 constexpr int COMBINE_BATCH_F32 = 8;
+constexpr int COMBINE_BATCH_SLICE = 16;  // loads per lane and batch, four splits per load
+constexpr int COMBINE_SLICES = 8;        // workgroups per row in the sliced combine (64 features each)
 constexpr int QSTAGE_PIECES = KV_DIM / 2 / 8;  // 36 16-byte pieces per row and half
 constexpr int QSTAGE_BYTES = ROWS_PER_WAVE * QSTAGE_PIECES * 16;  // 18 KB per wave
 constexpr int QSTAGE_LOADS = QSTAGE_BYTES / 1024;                 // 18 direct-to-LDS loads
@@ -92,6 +94,7 @@ struct Plan {
   int partial_blocks;  // multiple of 8
   int combine_wpr;     // waves per output row in the combine kernel (1, 2, 4, 8 or 16)
   int combine_halves;  // workgroups per row group (2: one per half of the features)
+  int combine_slices;  // 8: the sliced combine (a workgroup per row and 64 features), else 1
   int combine_blocks;
   size_t part_o_bytes;
   size_t ws_bytes;
@@ -1734,6 +1737,132 @@ __global__ __launch_bounds__((WPR < 4 ? 4 : WPR) * 64) void verify_attn_combine_
   }
 }
 
+// Combine for few rows (bf16 partials): one workgroup per (row, 64-feature
+// slice), so that a call with few rows still spreads the partial reads over
+// the device's CUs (each CU fetches rows of partials at a bounded rate). The
+// arithmetic is that of verify_attn_combine_kernel. Lane l reads features
+// 4 (l % 16) .. +3 of the slice (8 bytes) of split 4 (W j + w) + l / 16 of the
+// batch, so one load instruction covers four splits' 128-byte segments; wave
+// w takes splits 4 w .. 4 w + 3, 4 (W + w) .. of each batch of 4 W
+// COMBINE_BATCH_SLICE splits. Every lane keeps a running maximum, sum and four
+// feature sums over its own splits; the four lanes of a feature group are
+// then merged (lane xor 16, then xor 32: both lanes of a pair compute the same
+// products and sums, in commuted order, so they agree exactly) and the W waves'
+// results in wave order through LDS. Deterministic: the order depends only on
+// the plan.
+template <int W>
+__global__ __launch_bounds__(W * 64) void verify_attn_combine_slice_kernel(CombineArgs a) {
+  constexpr int BATCH = COMBINE_BATCH_SLICE;
+  __shared__ float red[W][16][6];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t grow = blockIdx.x / COMBINE_SLICES;
+  const int foff = (blockIdx.x % COMBINE_SLICES) * 64 + 4 * (lane & 15);
+  const int sl = lane >> 4;
+  if (grow >= (int64_t)a.B * a.M) return;  // workgroup-uniform
+  const int b = (int)(grow / a.M);
+  const int row = (int)(grow - (int64_t)b * a.M);
+  const uint16_t* part_o = static_cast<const uint16_t*>(a.part_o);
+
+  // One batch from split `first` (the lane's own first split): splits
+  // first + 4 W j, those at or past `limit` replaced by limit - 1 (loaded,
+  // never used): unconditional loads keep the compiler's waits per batch.
+  f32x2 ml[BATCH];
+  u32x2 ra[BATCH];
+  auto load = [&](int first, int limit) {
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int sp = min(first + 4 * W * j, limit - 1);
+      const int64_t rowid = (int64_t)sp * a.M + row;
+      ml[j] = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * rowid);
+      ra[j] = *reinterpret_cast<const u32x2*>(part_o + rowid * V_DIM + foff);
+    }
+  };
+
+  // Sequence 0's splits start at global split 0: its rows issue their first
+  // batch (bounded by max_splits, inside the workspace) before the split
+  // count is known; every other row locates its sequence's splits first.
+  int g0 = 0, g_end = 0;
+  if (b == 0) {
+    load(4 * wave + sl, a.max_splits);
+    const int len = clamp_len(a.seq_lens[0], a.T, a.max_seq_len);
+    g_end = (len + a.chunk - 1) / a.chunk;
+  } else {
+    SplitLoc loc;
+    if (locate_split(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, b, true, &loc)) {
+      g0 = loc.g0;
+      g_end = loc.g0 + loc.n_splits;
+    }
+  }
+  g_end = g_end < a.max_splits ? g_end : a.max_splits;
+  int first = g0 + 4 * wave + sl;
+  if (b != 0 && g0 + 4 * wave < g_end) load(first, g_end);  // wave-uniform
+
+  float mloc = -INFINITY, L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // wave-uniform loop bound: the wave's first split of the batch
+  for (int wbase = g0 + 4 * wave; wbase < g_end; wbase += 4 * W * BATCH) {
+    float mb = mloc;
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j)
+      if (first + 4 * W * j < g_end) mb = fmaxf(mb, ml[j][0]);
+    if (mb > mloc) {
+      const float sc = exp2f(mloc - mb);  // mloc = -inf -> 0
+      acc *= sc;
+      L *= sc;
+      mloc = mb;
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      if (first + 4 * W * j >= g_end || ml[j][0] == -INFINITY) continue;
+      const float w = exp2f(ml[j][0] - mloc) * ml[j][1];
+      acc += w * f32x4{bf16_lo(ra[j][0]), bf16_hi(ra[j][0]), bf16_lo(ra[j][1]), bf16_hi(ra[j][1])};
+      L += w;
+    }
+    first += 4 * W * BATCH;
+    if (wbase + 4 * W * BATCH < g_end) load(first, g_end);
+  }
+
+  // (m, L, acc) of two lanes or waves merged under their common maximum.
+  auto merge = [&](float m_o, float L_o, const f32x4& acc_o) {
+    const float mm = fmaxf(mloc, m_o);
+    const float s0 = mloc == -INFINITY ? 0.f : exp2f(mloc - mm);
+    const float s1 = m_o == -INFINITY ? 0.f : exp2f(m_o - mm);
+    acc = acc * s0 + acc_o * s1;
+    L = L * s0 + L_o * s1;
+    mloc = mm;
+  };
+#pragma unroll
+  for (int d = 16; d <= 32; d *= 2) {
+    const float m_o = __shfl_xor(mloc, d);
+    const float L_o = __shfl_xor(L, d);
+    f32x4 acc_o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc_o[k] = __shfl_xor(acc[k], d);
+    merge(m_o, L_o, acc_o);
+  }
+  if constexpr (W > 1) {
+    if (lane < 16) {
+      red[wave][lane][0] = mloc;
+      red[wave][lane][1] = L;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) red[wave][lane][2 + k] = acc[k];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 1; w < W; ++w)
+      merge(red[w][lane & 15][0], red[w][lane & 15][1],
+            f32x4{red[w][lane & 15][2], red[w][lane & 15][3], red[w][lane & 15][4], red[w][lane & 15][5]});
+  }
+  if (lane >= 16) return;
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  acc *= inv;
+  *reinterpret_cast<u32x2*>(a.out + grow * V_DIM + foff) =
+      u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+}
+
 // ------------------------------------------------------------ append kernel
 // Draft-row KV append: row (b, t) of kv_new -> kv_pool[slot of tree node t of
 // sequence b] (the last T entries of the sequence's slot_idx segment). One
@@ -1942,10 +2071,21 @@ int make_plan(const verify_attn_params* p, Plan* pl, DevShape dv, int rows_per_t
   int wpr = 1;
   const int64_t COMBINE_WAVES = COMBINE_WAVES_PER_CU * NUM_CUS;
   while (wpr < 16 && rows * wpr * 2 <= COMBINE_WAVES && wpr * 2 <= seq_splits) wpr *= 2;
-  // Few rows: split the features of a row over two workgroups, so that more
-  // CUs read the partials.
-  const int halves = (wpr == 16 && rows * 16 * 2 <= COMBINE_WAVES) ? 2 : 1;
-  const int64_t cblocks = ceil_div64(rows, (wpr < 4 ? 4 : wpr) / wpr) * halves;
+  // Few rows: split the features of a row over several workgroups, so that
+  // more CUs read the partials. Up to one row per 8 CUs on the bf16 path: the
+  // sliced combine (eight 64-feature slices, with the fewest waves, a power of
+  // two up to 16, that take a row's splits in one batch); with more rows its
+  // reads of the (max, sum) pairs, one cache line per split and workgroup,
+  // cost more than the spread gains. Else feature halves.
+  int halves = (wpr == 16 && rows * 16 * 2 <= COMBINE_WAVES) ? 2 : 1;
+  int slices = 1;
+  if (bf16_path && rows * 8 <= NUM_CUS) {
+    halves = 1;
+    slices = COMBINE_SLICES;
+    wpr = 1;
+    while (wpr < 16 && 4 * COMBINE_BATCH_SLICE * wpr < seq_splits) wpr *= 2;
+  }
+  const int64_t cblocks = slices > 1 ? rows * slices : ceil_div64(rows, (wpr < 4 ? 4 : wpr) / wpr) * halves;
   if (blocks > INT32_MAX || cblocks > INT32_MAX || max_splits > INT32_MAX || chunk > INT32_MAX)
     return VERIFY_ATTN_ERR_BAD_DIM;
   pl->M = (int)M;
@@ -1958,6 +2098,7 @@ int make_plan(const verify_attn_params* p, Plan* pl, DevShape dv, int rows_per_t
   pl->partial_blocks = (int)blocks;
   pl->combine_wpr = wpr;
   pl->combine_halves = halves;
+  pl->combine_slices = slices;
   pl->combine_blocks = (int)cblocks;
   // V averages: bf16 on the bf16 path, fp32 on the fp32-input path
   pl->part_o_bytes = (size_t)max_splits * (size_t)M * V_DIM * (bf16_path ? 2 : 4);
@@ -2043,7 +2184,17 @@ int launch_combine(const verify_attn_params* p, const Plan& pl, const int32_t* s
       default: VA_COMBINE(1, true); break;
     }
   } else {
-    if (pl.combine_halves == 2) hipLaunchKernelGGL((verify_attn_combine_kernel<16, false, true>), grid, dim3(16 * 64), 0, stream, a);
+    if (pl.combine_slices > 1) {
+#define VA_SLICE(W) hipLaunchKernelGGL((verify_attn_combine_slice_kernel<W>), grid, dim3(W * 64), 0, stream, a)
+      switch (pl.combine_wpr) {
+        case 16: VA_SLICE(16); break;
+        case 8: VA_SLICE(8); break;
+        case 4: VA_SLICE(4); break;
+        case 2: VA_SLICE(2); break;
+        default: VA_SLICE(1); break;
+      }
+#undef VA_SLICE
+    } else if (pl.combine_halves == 2) hipLaunchKernelGGL((verify_attn_combine_kernel<16, false, true>), grid, dim3(16 * 64), 0, stream, a);
     else switch (pl.combine_wpr) {
       case 16: VA_COMBINE(16, false); break;
       case 8: VA_COMBINE(8, false); break;

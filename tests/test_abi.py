@@ -362,12 +362,16 @@ def test_binding_refuses_tensors_on_another_device():
 
 def test_plan_row_kernel_bands():
     """Rows per sequence pick the kernel: at most 32 the small-row kernel (64-key
-    tiles, one row tile), more the 128-row kernel (32-key tiles)."""
+    tiles, one row tile), more the 128-row kernel (32-key tiles). On a 256-CU
+    device a call of at most 32 rows also takes the sliced combine (eight
+    workgroups per row); more rows take at most two per row."""
     for H, T in [(1, 1), (8, 1), (8, 4), (4, 8), (16, 2), (3, 11), (8, 5), (8, 9), (16, 5), (8, 10),
                  (1, 64), (81, 1), (8, 11), (16, 8), (64, 64)]:
         M = H * T
         plan = mtv.verify_attn_plan(base_params(num_heads=H, tree_size=T))
         if M <= 32:
             assert plan["keys_per_tile"] == 64 and plan["row_tiles"] == 1 and plan["rows_per_tile"] == M, (H, T, plan)
+            assert plan["combine_blocks"] == 8 * M, (H, T, plan)
         else:
             assert plan["keys_per_tile"] == 32 and plan["rows_per_tile"] == 128, (H, T, plan)
+            assert plan["combine_blocks"] <= 2 * M, (H, T, plan)

@@ -276,8 +276,9 @@ def test_nsplit_independent(orc, nsplit):
 @pytest.mark.parametrize("case", [
     dict(B=1, H=64, T=64, prefixes=[6000], nsplit=40),           # 4096 rows, one wave per row
     dict(B=3, H=64, T=16, prefixes=[3000, 0, 5000], nsplit=48),  # rows of sequences 1 and 2 locate their splits
-    dict(B=1, H=8, T=1, prefixes=[60000], nsplit=600),           # 8 rows: half rows, 16 waves per row
+    dict(B=1, H=8, T=1, prefixes=[60000], nsplit=600),           # 8 rows: the sliced combine
     dict(B=2, H=8, T=2, prefixes=[30000, 20000], nsplit=800),
+    dict(B=1, H=8, T=9, prefixes=[60000], nsplit=600),           # 72 rows: half rows, 16 waves per row
 ], ids=lambda c: "B{B}_H{H}_T{T}_n{nsplit}".format(**c))
 def test_combine_batches(orc, case):
     """Splits enough that every combine wave takes several batches of loads
@@ -290,6 +291,27 @@ def test_combine_batches(orc, case):
     c = plan["keys_per_split"]
     per_seq = [-(-(p + wl.T) // c) for p in case["prefixes"]]
     assert max(per_seq) > 16 * 16 or (wl.H * wl.T * case["B"] > 2048 and max(per_seq) > 12), per_seq
+    check_full(orc, wl, nsplit=nsplit)
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=1, H=8, T=1, prefixes=[140000], nsplit=2200),                # 16 waves, three batches each
+    dict(B=4, H=2, T=4, prefixes=[9000, 0, 3000, 20000], nsplit=300),   # sequences 1-3 locate their splits
+    dict(B=1, H=4, T=2, prefixes=[700], nsplit=0),                      # one wave per workgroup
+    dict(B=2, H=16, T=1, prefixes=[40000, 1], nsplit=0),                # 32 rows, one sequence of one split
+], ids=lambda c: "B{B}_H{H}_T{T}_n{nsplit}".format(**c))
+def test_sliced_combine(orc, case):
+    """Calls of at most 32 rows take the sliced combine (a workgroup per row
+    and 64 features, four splits per load instruction): full-output parity
+    with one to sixteen waves per workgroup, several batches per wave, and
+    rows of later sequences that locate their splits."""
+    import mla_tree_verify_latent_amd as mtv
+    case = dict(case)
+    nsplit = case.pop("nsplit")
+    wl = small("sliced", pool=sum(case["prefixes"]) + case["B"] * case["T"] + 300, seed=23, **case)
+    assert wl.B * wl.H * wl.T <= 32
+    plan = mtv.verify_attn_plan(params_of(wl, nsplit))
+    assert plan["combine_blocks"] == 8 * wl.B * wl.H * wl.T
     check_full(orc, wl, nsplit=nsplit)
 
 
