@@ -2074,9 +2074,8 @@ int make_plan(const verify_attn_params* p, Plan* pl, DevShape dv, int rows_per_t
   // Few rows: split the features of a row over several workgroups, so that
   // more CUs read the partials. Up to one row per 8 CUs on the bf16 path: the
   // sliced combine (eight 64-feature slices, with the fewest waves, a power of
-  // two up to 16, that take a row's splits in one batch); with more rows its
-  // reads of the (max, sum) pairs, one cache line per split and workgroup,
-  // cost more than the spread gains. Else feature halves.
+  // two up to 16, that take a row's splits in one batch); with more rows it
+  // measured no faster, and at 128 or more rows slower. Else feature halves.
   int halves = (wpr == 16 && rows * 16 * 2 <= COMBINE_WAVES) ? 2 : 1;
   int slices = 1;
   if (bf16_path && rows * 8 <= NUM_CUS) {
