@@ -811,28 +811,51 @@ void verify_attn_partial_kernel(PartialArgs a) {
     pv_tile(it);
     sv = sn;
   }
-  wait_vmcnt<0>();  // no load outlives the workgroup
+  wait_vmcnt<0>();  // no load outlives the workgroup, and no gather lands in LDS after this
   mfma_drain();     // O is read below
+  lds_barrier();    // every wave is done with the tile buffers, which now stage the partial rows
 
   if (!wave_active) return;
-  // ---- partial results of this split
-  const float l_row = l_run + xor32(l_run);
-  if (row_ok) {
-    // the split's V average (0 for a row with every key of the split masked)
-    const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
-    const int64_t rowid = (int64_t)g * a.M + qrow;
-    uint16_t* po = a.part_o + rowid * V_DIM + 4 * hl;
+  // ---- partial results of this split: the V average (0 for a row with every
+  // key of the split masked), rounded to bf16, and the running maximum and sum.
+  // The lane holds 4 features of each 8-feature chunk of its row; the wave's
+  // 32 rows pass through LDS (row r: 1 KB, chunk c at position c ^ r, so that
+  // the writes of 32 rows and the reads of one row are free of bank conflicts)
+  // and leave one row per store instruction, 1 KB contiguous.
+  // The lane's row and half are formed anew here (an asm statement the
+  // compiler neither hoists nor merges), so that nothing derived from the lane
+  // index has to stay live across the loop.
+  int el;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(el));
+  const int er = el & 31, ehl = el >> 5;
+  const bool erow_ok = row0 + er < a.M;
+  float l_row;
+  {  // l_run + xor32(l_run), with the lane half taken from el
+    const unsigned u = __builtin_bit_cast(unsigned, l_run);
+    const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    l_row = l_run + __builtin_bit_cast(float, ehl ? sw[0] : sw[1]);
+  }
+  const float inv = (erow_ok && l_row > 0.f) ? 1.0f / l_row : 0.f;
+  const uint32_t stage = smem_base + wave * (ROWS_PER_WAVE * V_DIM * 2);
 #pragma unroll
-    for (int cb = 0; cb < PV_BLOCKS; ++cb)
+  for (int cb = 0; cb < PV_BLOCKS; ++cb)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        *reinterpret_cast<u32x2*>(po + 32 * cb + 8 * i4) =
-            u32x2{pack_bf16x2(o[cb][4 * i4] * inv, o[cb][4 * i4 + 1] * inv),
-                  pack_bf16x2(o[cb][4 * i4 + 2] * inv, o[cb][4 * i4 + 3] * inv)};
-    if (hl == 0) {
-      a.part_ml[2 * rowid] = m_run;
-      a.part_ml[2 * rowid + 1] = l_row;
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int c = 4 * cb + i4;  // features 8c + 4 hl .. +3
+      *(LDS_AS u32x2*)(uintptr_t)(stage + er * (V_DIM * 2) + ((c ^ er) << 4) + 8 * ehl) =
+          u32x2{pack_bf16x2(o[cb][4 * i4] * inv, o[cb][4 * i4 + 1] * inv),
+                pack_bf16x2(o[cb][4 * i4 + 2] * inv, o[cb][4 * i4 + 3] * inv)};
     }
+  const int nrows = min(ROWS_PER_WAVE, a.M - row0);  // wave-uniform, >= 1
+  uint16_t* po = a.part_o + ((int64_t)g * a.M + row0) * V_DIM + 8 * el;
+  for (int r = 0; r < nrows; ++r) {
+    const u32x4 v = *(const LDS_AS u32x4*)(uintptr_t)(stage + r * (V_DIM * 2) + ((el ^ r) << 4));
+    *reinterpret_cast<u32x4*>(po + (int64_t)r * V_DIM) = v;
+  }
+  if (erow_ok && ehl == 0) {
+    const int64_t rowid = (int64_t)g * a.M + row0 + er;
+    a.part_ml[2 * rowid] = m_run;
+    a.part_ml[2 * rowid + 1] = l_row;
   }
 }
 
@@ -1327,22 +1350,36 @@ void verify_attn_partial_small_kernel(PartialArgs a) {
     if (grp == 0) *(LDS_AS float*)(uintptr_t)(rmax_base + ((16 * rb + l16) * NWAVES + wave) * 4) = t;
   }
   lds_barrier();
+  // The bf16 averages pass through LDS (tile 0's buffer, free since the loop
+  // ended): local row lr takes 1 KB, 16-byte chunk c at position c ^ (lr % 64),
+  // so that a wave's writes (16 rows x two chunks) and the reads of one row are
+  // free of bank conflicts; each row then leaves with one 1 KB store.
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     if (!row_ok[rb]) continue;
     const f32x4 wl = *(const LDS_AS f32x4*)(uintptr_t)(rmax_base + (16 * rb + l16) * NWAVES * 4);
     const float t = (wl[0] + wl[1]) + (wl[2] + wl[3]);
     const float inv = t > 0.f ? 1.0f / t : 0.f;
-    const int64_t rowid = (int64_t)g * a.M + qrow[rb];
-    uint16_t* po = a.part_o + rowid * V_DIM + wave * 128 + 4 * grp;
+    const int lr = 16 * rb + l16;
 #pragma unroll
-    for (int fb = 0; fb < SM_FB; ++fb)
-      *reinterpret_cast<u32x2*>(po + 16 * fb) = u32x2{pack_bf16x2(o[fb][rb][0] * inv, o[fb][rb][1] * inv),
-                                                      pack_bf16x2(o[fb][rb][2] * inv, o[fb][rb][3] * inv)};
+    for (int fb = 0; fb < SM_FB; ++fb) {
+      const int c = 16 * wave + 2 * fb + (grp >> 1);  // features 128 wave + 16 fb + 4 grp .. +3
+      *(LDS_AS u32x2*)(uintptr_t)(smem_base + lr * (V_DIM * 2) + ((c ^ lr) << 4) + 8 * (grp & 1)) =
+          u32x2{pack_bf16x2(o[fb][rb][0] * inv, o[fb][rb][1] * inv),
+                pack_bf16x2(o[fb][rb][2] * inv, o[fb][rb][3] * inv)};
+    }
     if (wave == 0 && grp == 0) {
+      const int64_t rowid = (int64_t)g * a.M + qrow[rb];
       a.part_ml[2 * rowid] = m_run[rb];
       a.part_ml[2 * rowid + 1] = t;
     }
+  }
+  lds_barrier();
+  const int nrows = min(rpt, a.M - rt * rpt);  // valid local rows: 0 .. nrows-1
+  uint16_t* po = a.part_o + ((int64_t)g * a.M + rt * rpt) * V_DIM + 8 * lane;
+  for (int lr = wave; lr < nrows; lr += NWAVES) {
+    const u32x4 v = *(const LDS_AS u32x4*)(uintptr_t)(smem_base + lr * (V_DIM * 2) + ((lane ^ lr) << 4));
+    *reinterpret_cast<u32x4*>(po + (int64_t)lr * V_DIM) = v;
   }
 }
 
