@@ -79,7 +79,30 @@ def algorithmic_flops(wl) -> int:
 
 
 def kernel_source_digest() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments removed and whitespace runs
+    collapsed (string and character literals kept as written), so that counter
+    files stay matched to the code they were taken on across comment edits."""
+    text = open(KERNEL_SRC, encoding="utf-8").read()
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    code = " ".join("".join(out).split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 class Bench:

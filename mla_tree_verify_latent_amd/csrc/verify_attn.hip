@@ -819,9 +819,9 @@ void verify_attn_partial_kernel(PartialArgs a) {
   // ---- partial results of this split: the V average (0 for a row with every
   // key of the split masked), rounded to bf16, and the running maximum and sum.
   // The lane holds 4 features of each 8-feature chunk of its row; the wave's
-  // 32 rows pass through LDS (row r: 1 KB, chunk c at position c ^ r, so that
-  // the writes of 32 rows and the reads of one row are free of bank conflicts)
-  // and leave one row per store instruction, 1 KB contiguous.
+  // 32 rows pass through LDS (row r: 1 KB, chunk c at position c ^ r, which
+  // spreads the writes of 32 rows and the reads of one row evenly over the
+  // banks) and leave one row per store instruction, 1 KB contiguous.
   // The lane's row and half are formed anew here (an asm statement the
   // compiler neither hoists nor merges), so that nothing derived from the lane
   // index has to stay live across the loop.
@@ -1352,8 +1352,8 @@ void verify_attn_partial_small_kernel(PartialArgs a) {
   lds_barrier();
   // The bf16 averages pass through LDS (tile 0's buffer, free since the loop
   // ended): local row lr takes 1 KB, 16-byte chunk c at position c ^ (lr % 64),
-  // so that a wave's writes (16 rows x two chunks) and the reads of one row are
-  // free of bank conflicts; each row then leaves with one 1 KB store.
+  // which spreads a wave's writes (16 rows x two chunks) and the reads of one
+  // row evenly over the banks; each row then leaves with one 1 KB store.
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     if (!row_ok[rb]) continue;

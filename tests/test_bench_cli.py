@@ -26,3 +26,20 @@ def test_kernel_stats_summary(tmp_path):
     lines = r.stdout.strip().splitlines()
     assert lines[0].startswith("| kernel | calls | average us")
     assert "| 10 | 80.00 | 79.00 | 81.00 | 90.0% |" in lines[2]
+
+
+def test_kernel_source_digest_follows_code_not_comments(tmp_path, monkeypatch):
+    """The hash that ties counter files to the kernel source ignores comments and
+    whitespace but changes with any code token, string literals included."""
+    sys.path.insert(0, ROOT)
+    import bench
+    def digest(text):
+        f = tmp_path / "k.hip"
+        f.write_text(text)
+        monkeypatch.setattr(bench, "KERNEL_SRC", str(f))
+        return bench.kernel_source_digest()
+    base = 'int f(int x) {  // scale\n  return x * 2; /* twice */\n}\nconst char* s = "a // b";\n'
+    same = '// header\nint f(int x) {\n    return x * 2;\n}\n/* block\n comment */ const char* s = "a // b";\n'
+    assert digest(base) == digest(same)
+    assert digest(base) != digest(base.replace("x * 2", "x * 3"))
+    assert digest(base) != digest(base.replace('"a // b"', '"a / b"'))
