@@ -1594,28 +1594,41 @@ void verify_attn_f32_partial_kernel(PartialF32Args a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  wait_vmcnt<0>();
+  wait_vmcnt<0>();  // no gather lands in LDS after this
   mfma_drain();
+  lds_barrier();    // every wave is done with the tile buffers, which now stage the partial rows
 
   if (!wave_active) return;
   // l: the four lane groups of a row hold disjoint keys
   float l_row = l_run + __shfl_xor(l_run, 16);
   l_row += __shfl_xor(l_row, 32);
-  if (row_ok) {
-    // the split's V average (0 for a row with every key of the split masked)
-    const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
-    const int64_t rowid = (int64_t)g * a.M + qrow;
-    float* po = a.part_o + rowid * V_DIM + 4 * grp;
+  // The split's V average (0 for a row with every key of the split masked)
+  // leaves through LDS in two halves of 256 features: the wave's 16 rows take
+  // 1 KB each (16-byte chunk c at position c ^ row), and each row half then
+  // leaves with one contiguous 1 KB store.
+  const float inv = (row_ok && l_row > 0.f) ? 1.0f / l_row : 0.f;
+  const uint32_t stage = smem_base + wave * (F_ROWS_PER_WAVE * 1024);
+  const int nrows = min(F_ROWS_PER_WAVE, a.M - row0);  // wave-uniform, >= 1
+  float* po = a.part_o + ((int64_t)g * a.M + row0) * V_DIM + 4 * lane;
 #pragma unroll
-    for (int J = 0; J < F_PV_BLOCKS / 4; ++J)
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)  // feature 64 J + 16 grp + 4 j
-        *reinterpret_cast<f32x4*>(po + 64 * J + 12 * grp + 4 * j) =
+    for (int J = 4 * half; J < 4 * half + 4; ++J)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // features 64 J + 16 grp + 4 j .. +3: chunk c of the half
+        const int c = 16 * (J - 4 * half) + 4 * grp + j;
+        *(LDS_AS f32x4*)(uintptr_t)(stage + l16 * 1024 + ((c ^ l16) << 4)) =
             f32x4{o[4 * J][j], o[4 * J + 1][j], o[4 * J + 2][j], o[4 * J + 3][j]} * inv;
-    if (grp == 0) {
-      a.part_ml[2 * rowid] = m_run;
-      a.part_ml[2 * rowid + 1] = l_row;
+      }
+    for (int r = 0; r < nrows; ++r) {
+      const f32x4 v = *(const LDS_AS f32x4*)(uintptr_t)(stage + r * 1024 + ((lane ^ r) << 4));
+      *reinterpret_cast<f32x4*>(po + (int64_t)r * V_DIM + 256 * half) = v;
     }
+  }
+  if (row_ok && grp == 0) {
+    const int64_t rowid = (int64_t)g * a.M + qrow;
+    a.part_ml[2 * rowid] = m_run;
+    a.part_ml[2 * rowid + 1] = l_row;
   }
 }
 
