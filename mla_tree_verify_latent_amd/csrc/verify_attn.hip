@@ -2088,6 +2088,11 @@ int make_plan(const verify_attn_params* p, Plan* pl, DevShape dv, int rows_per_t
     // tile of partial traffic (written, then read by the combine). More, shorter
     // splits fill the last round better but add fixed costs and partials.
     const int64_t split_cap = ceil_div64(p->max_seq_len, nk) * nk;  // one split per sequence
+    // The 128-row kernel also tries longer splits (up to 4x) for each round
+    // count: its workgroups each stage 147 KB of query and store 128 rows of
+    // partials, so fewer, longer splits can win within the same rounds. The
+    // small-row kernel's items are cheap, and its shortest split measured best.
+    const int64_t widen = (bf16_path && rows_per_tile == ROWS_PER_TILE) ? 4 : 1;
     const int64_t floor_c = nk;
     // fewest rounds with room for every sequence's last split
     const int64_t r0 = ceil_div64((int64_t)p->num_seqs * row_tiles, NUM_CUS);
@@ -2098,11 +2103,13 @@ int make_plan(const verify_attn_params* p, Plan* pl, DevShape dv, int rows_per_t
       int64_t c = ceil_div64(p->total_kv, splits);
       c = ceil_div64(c, nk) * nk;
       if (c > split_cap) c = split_cap;
-      const int64_t items = (ceil_div64(p->total_kv, c) + p->num_seqs - 1) * row_tiles;
-      const int64_t cost = ceil_div64(items, NUM_CUS) * (20 * (c / nk) + 20 * ROUND_COST_TILES) + items;
-      if (cost < best_cost) {
-        best_cost = cost;
-        best = c;
+      for (int64_t cc = c; cc <= widen * c && cc <= split_cap; cc += nk) {
+        const int64_t items = (ceil_div64(p->total_kv, cc) + p->num_seqs - 1) * row_tiles;
+        const int64_t cost = ceil_div64(items, NUM_CUS) * (20 * (cc / nk) + 20 * ROUND_COST_TILES) + items;
+        if (cost < best_cost) {
+          best_cost = cost;
+          best = cc;
+        }
       }
       if (c <= floor_c) break;  // more rounds cannot shorten the split further
     }
