@@ -302,6 +302,24 @@ __device__ bool locate_item(const int32_t* __restrict__ seq_lens, int B, int T, 
   return true;
 }
 
+// Work item of a partial-kernel workgroup when the batch holds one sequence:
+// the (split, row tile) items of a sequence max_len keys long, dealt to the
+// XCDs as in locate_item. No device read, so the workgroup can issue its first
+// loads before the sequence's length arrives; it ends once the length shows
+// its split empty (lengths below max_len).
+__device__ __forceinline__ bool deal_single(int max_len, int chunk, int max_splits, int row_tiles,
+                                            int nxcd, int* g_out, int* rt_out) {
+  const int ns = (max_len + chunk - 1) / chunk;
+  const int n_items = min(ns, max_splits) * row_tiles;
+  const int per_xcd = (n_items + nxcd - 1) / nxcd;
+  const int k_on_xcd = blockIdx.x / nxcd;
+  const int logical = (blockIdx.x - k_on_xcd * nxcd) * per_xcd + k_on_xcd;
+  if (k_on_xcd >= per_xcd || logical >= n_items) return false;
+  *g_out = logical / row_tiles;
+  *rt_out = logical - *g_out * row_tiles;
+  return true;
+}
+
 // Swizzle of the 16-byte chunk position inside a 128-byte row segment:
 // position = (c % 8) ^ swz(row), where swz swaps bits 1 and 2 of row % 8 and
 // flips bit 0 for rows 16..31 of a tile. Both operand access patterns of the
@@ -464,6 +482,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast
 // wave being done with iteration it-1, frees tile it-1's buffer for the gather
 // of tile it+3, whose nine loads ride on the first half of the QK MFMAs (one
 // every two), so the last of them has the rest of QK and all of PV to land.
+template <bool ONE_SEQ>
 __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void verify_attn_partial_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * TILE_BYTES + SLOT_RING * NWAVES * 256];
@@ -472,9 +491,24 @@ void verify_attn_partial_kernel(PartialArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
+  // ONE_SEQ (a batch of one sequence): the item comes from deal_single, and
+  // the sequence's length and the slot entry of the split's first key are
+  // loaded beside the first slot-table and query loads; until the length is
+  // in, the split's end is bounded by max_seq_len. Otherwise locate_item.
   int g, rt;
   SplitLoc loc;
-  if (!locate_item(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, a.max_splits, a.row_tiles, a.nxcd, &g, &rt, &loc)) return;
+  int len_first = 0, slot_first = 0;
+  if constexpr (ONE_SEQ) {
+    if (!deal_single(a.max_seq_len, a.chunk, a.max_splits, a.row_tiles, a.nxcd, &g, &rt)) return;
+    loc.b = 0;
+    loc.g0 = 0;
+    loc.n_splits = 0;
+    loc.len = a.max_seq_len;
+    loc.seg = 0;
+  } else {
+    if (!locate_item(a.seq_lens, a.B, a.T, a.max_seq_len, a.chunk, a.max_splits, a.row_tiles, a.nxcd, &g, &rt, &loc))
+      return;
+  }
   g = __builtin_amdgcn_readfirstlane(g);
   rt = __builtin_amdgcn_readfirstlane(rt);
   loc.b = __builtin_amdgcn_readfirstlane(loc.b);
@@ -484,8 +518,14 @@ void verify_attn_partial_kernel(PartialArgs a) {
             (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)loc.seg);
   const int split = g - loc.g0;
   const int k0 = split * a.chunk;
-  const int k1 = min(k0 + a.chunk, loc.len);
-  const int P = loc.len - a.T;
+  int k1 = min(k0 + a.chunk, loc.len);
+  int P = loc.len - a.T;
+  if constexpr (ONE_SEQ) {
+    // vector loads (a uniform address): their wait is counted with the
+    // prologue's other loads
+    len_first = a.seq_lens[0];
+    slot_first = a.slot_idx[k0 < a.total_kv ? k0 : a.total_kv - 1];
+  }
 
   // ---- KV gather addressing
   const int ld_row = wave * ROWS_PER_LOAD_WAVE + (lane >> 3);
@@ -572,6 +612,24 @@ void verify_attn_partial_kernel(PartialArgs a) {
   // A wave without query rows skips the staging loads (its reads are then
   // replaced by zeros above; the waits below only get looser).
   if (wave_active) q_stage(0);
+
+  if constexpr (ONE_SEQ) {
+    // With the length in: a split past the sequence's end leaves (once its
+    // loads have landed: the query staging writes LDS); rows of tiles 0 and 1
+    // past the end take the split's first key's slot, so that only this
+    // sequence's KV rows are read (they are masked like the repeated last row
+    // of a short split).
+    loc.len = clamp_len(len_first, a.T, a.max_seq_len);
+    if (k0 >= loc.len) {
+      wait_vmcnt<0>();
+      return;
+    }
+    k1 = min(k0 + a.chunk, loc.len);
+    P = loc.len - a.T;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      if (k0 + t * NK + wave * ROWS_PER_LOAD_WAVE + (lane >> 3) >= k1) s_pro[t] = slot_first;
+  }
 
   // Steady-state load order (iteration i: slots of tile i+5, gather of tile
   // i+3) for i = -3, -2: the gathers of tiles 0 and 1. Forming their row
@@ -2209,8 +2267,10 @@ int launch_partial(const verify_attn_params* p, const Plan& pl, const void* q, c
     hipLaunchKernelGGL(verify_attn_partial_small_kernel<1>, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
   else if (pl.rows_per_tile <= SM_ROWS)
     hipLaunchKernelGGL(verify_attn_partial_small_kernel<2>, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
+  else if (p->num_seqs == 1)
+    hipLaunchKernelGGL(verify_attn_partial_kernel<true>, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL(verify_attn_partial_kernel, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
+    hipLaunchKernelGGL(verify_attn_partial_kernel<false>, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
   return hipGetLastError() == hipSuccess ? VERIFY_ATTN_OK : VERIFY_ATTN_ERR_LAUNCH_FAILED;
 }
 
