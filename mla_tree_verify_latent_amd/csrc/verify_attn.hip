@@ -588,9 +588,12 @@ void verify_attn_partial_kernel(PartialArgs a) {
   // r + 16 on positions that differ in bit 0 (the rules of swz above).
   const uint32_t qstage = smem_base + 2 * TILE_BYTES + wave * QSTAGE_BYTES;
   auto qswz = [](int r) { return ((r >> 1) & 3) ^ ((r >> 4) & 1); };
+  // Loads whose first row is past M are skipped (they would only repeat row
+  // 0; the waits below count younger loads only, so they just get looser).
   auto q_stage = [&](int half) {
 #pragma unroll
     for (int j = 0; j < QSTAGE_LOADS; ++j) {
+      if (row0 + (j * 64) / QSTAGE_PIECES >= a.M) continue;  // wave-uniform
       const int slot = j * 64 + lane;
       const int r = slot / QSTAGE_PIECES;
       const int p = (slot - r * QSTAGE_PIECES) ^ qswz(r);
