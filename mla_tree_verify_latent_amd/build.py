@@ -49,8 +49,10 @@ def check_registers(extra=()) -> dict:
     # bf16 kernel: 256 output accumulators; fp32 kernel: 128 (the compiler may
     # round the AGPR block up). Neither may spill.
     # small-row kernel: its query block (72 or 144 registers) in AGPRs.
-    need = {"verify_attn_partial_kernelILb0E": lambda n: n == 256,  # several sequences
-            "verify_attn_partial_kernelILb1E": lambda n: n == 256,  # one sequence
+    need = {"verify_attn_partial_kernelILb0ELb0E": lambda n: n == 256,  # several sequences
+            "verify_attn_partial_kernelILb0ELb1E": lambda n: n == 256,  # several, idle waves
+            "verify_attn_partial_kernelILb1ELb0E": lambda n: n == 256,  # one sequence
+            "verify_attn_partial_kernelILb1ELb1E": lambda n: n == 256,  # one, idle waves
             "verify_attn_partial_small_kernelILi1E": lambda n: n >= 72,
             "verify_attn_partial_small_kernelILi2E": lambda n: n >= 144,
             "verify_attn_f32_partial_kernelE": lambda n: n >= 128}

@@ -482,7 +482,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast
 // wave being done with iteration it-1, frees tile it-1's buffer for the gather
 // of tile it+3, whose nine loads ride on the first half of the QK MFMAs (one
 // every two), so the last of them has the rest of QK and all of PV to land.
-template <bool ONE_SEQ>
+template <bool ONE_SEQ, bool IDLE_WAVES>
 __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void verify_attn_partial_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * TILE_BYTES + SLOT_RING * NWAVES * 256];
@@ -569,8 +569,8 @@ void verify_attn_partial_kernel(PartialArgs a) {
   for (int t = 0; t < 2; ++t) s_pro[t] = *slot_ptr(k0 + t * NK, lane >> 3);
   // Query fragments (B operand of S^T = K Q^T): lane l holds row l%32,
   // features 16 ks + 8 (l/32) .. +7 of k-step ks, i.e. 16-byte piece
-  // 2 ks + l/32 of its row. Waves without query rows run the same schedule on
-  // zeros (they still gather their share of the KV).
+  // 2 ks + l/32 of its row. A wave without query rows only gathers its share
+  // of the KV (see the loop below).
   const int row0 = rt * ROWS_PER_TILE + wave * ROWS_PER_WAVE;
   const bool wave_active = row0 < a.M;  // wave-uniform
   const int qrow = row0 + (lane & 31);
@@ -840,6 +840,31 @@ void verify_attn_partial_kernel(PartialArgs a) {
     }
   };
 
+  // IDLE_WAVES (some row tile holds at most 96 rows): a wave without query
+  // rows runs no MFMA. It only gathers its share of every tile, with the same
+  // loads, waits and barriers as the loop below, and leaves after the last
+  // barrier. (Without idle waves the instance keeps the loop's code as it is.)
+  if (IDLE_WAVES && !wave_active) {
+    auto gather_only = [&](int t) {  // the loads qk_tile(t) issues
+      const int slot_next = ring_slot(t + 2);
+      const uint32_t gdst = gather_dst(t + 2);
+      issue_slots(t + 4);
+      const uint16_t* gsrc = gather_src(slot_next);
+#pragma unroll
+      for (int j = 0; j < CHUNK_GROUPS; ++j) load_to_lds16(gsrc + 64 * j, gdst + j * GROUP_BYTES);
+    };
+    lds_barrier();
+    gather_only(0);
+    for (int it = 0; it + 1 < ntiles; ++it) {
+      wait_vmcnt<CHUNK_GROUPS + 1>();
+      lds_barrier();
+      gather_only(it + 1);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();  // the epilogue's barrier
+    return;
+  }
+
   // Tile 0: publish it (every load of this wave so far has landed; the
   // barrier also ends every wave's query reads from the staging region),
   // then its QK (carrying the gather of tile 2).
@@ -875,8 +900,7 @@ void verify_attn_partial_kernel(PartialArgs a) {
   wait_vmcnt<0>();  // no load outlives the workgroup, and no gather lands in LDS after this
   mfma_drain();     // O is read below
   lds_barrier();    // every wave is done with the tile buffers, which now stage the partial rows
-
-  if (!wave_active) return;
+  if (!IDLE_WAVES && !wave_active) return;
   // ---- partial results of this split: the V average (0 for a row with every
   // key of the split masked), rounded to bf16, and the running maximum and sum.
   // The lane holds 4 features of each 8-feature chunk of its row; the wave's
@@ -2270,10 +2294,16 @@ int launch_partial(const verify_attn_params* p, const Plan& pl, const void* q, c
     hipLaunchKernelGGL(verify_attn_partial_small_kernel<1>, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
   else if (pl.rows_per_tile <= SM_ROWS)
     hipLaunchKernelGGL(verify_attn_partial_small_kernel<2>, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
-  else if (p->num_seqs == 1)
-    hipLaunchKernelGGL(verify_attn_partial_kernel<true>, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL(verify_attn_partial_kernel<false>, dim3(pl.partial_blocks), dim3(NWAVES * 64), 0, stream, a);
+  else {
+    // some row tile holds at most 96 rows: a wave may have none
+    const int last = pl.M - (pl.row_tiles - 1) * ROWS_PER_TILE;
+    const bool idle = last <= ROWS_PER_TILE - ROWS_PER_WAVE;
+    const dim3 grid(pl.partial_blocks), block(NWAVES * 64);
+    if (p->num_seqs == 1 && idle) hipLaunchKernelGGL((verify_attn_partial_kernel<true, true>), grid, block, 0, stream, a);
+    else if (p->num_seqs == 1) hipLaunchKernelGGL((verify_attn_partial_kernel<true, false>), grid, block, 0, stream, a);
+    else if (idle) hipLaunchKernelGGL((verify_attn_partial_kernel<false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((verify_attn_partial_kernel<false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError() == hipSuccess ? VERIFY_ATTN_OK : VERIFY_ATTN_ERR_LAUNCH_FAILED;
 }
 
