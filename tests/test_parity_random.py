@@ -76,3 +76,53 @@ def test_random_shape_f32(orc, case):
     wl = _workload(case, dtype="f32")
     ok, worst, row = rel_gate(run_gpu_f32(wl, case["nsplit"]), orc.run(wl))
     assert ok, f"row {row} at {worst:.2e} of the row scale"
+
+
+def draw_loose(n, seed):
+    """Shapes whose host-side bounds run past the data: max_seq_len above every
+    length and the slot table longer than the sequences, its extra entries
+    naming pool rows of NaNs."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        B = int(rng.choice([1, 1, 2, 3]))
+        H = int(rng.choice([1, 2, 4, 8, 16, 64]))
+        T = int(rng.integers(1, 65))
+        prefixes = [int(x) for x in rng.integers(0, 3000, size=B)]
+        if H * T * sum(p + T for p in prefixes) > MAX_PAIRS:
+            continue
+        bound = int(rng.integers(1, 4000))
+        out.append(dict(B=B, H=H, T=T, prefixes=prefixes, nsplit=int(rng.choice([0, 0, 3, 11])),
+                        tree="random", seed=9000 + len(out), bound=bound,
+                        extra=min(int(rng.integers(1, 600)), bound)))  # total_kv <= B * max_seq_len
+    return out
+
+
+SHAPES_LOOSE = draw_loose(16, 77)
+
+
+@pytest.mark.parametrize("case", SHAPES_LOOSE, ids=lambda c: _id(c) + "_b{bound}_x{extra}".format(**c))
+def test_random_loose_bounds(orc, case):
+    """Every kernel path (one or several sequences, small-row and 128-row
+    kernels, idle waves, the sliced combine) with a loose max_seq_len and
+    slot-table entries past the sequences that point at NaN rows: the output
+    stays finite and within the gate of the unextended inputs."""
+    import torch
+    import mla_tree_verify_latent_amd as mtv
+    from helpers import bf16_out_to_f32, to_device
+    wl = _workload(case)
+    dev = to_device(wl)
+    x = case["extra"]
+    dev["kv_pool"] = torch.cat([dev["kv_pool"], torch.full((x, 576), float("nan"), dtype=torch.bfloat16,
+                                                           device="cuda")])
+    dev["slot_idx"] = torch.cat([dev["slot_idx"], torch.arange(wl.pool_slots, wl.pool_slots + x,
+                                                               dtype=torch.int32, device="cuda")])
+    prm = mtv.make_params(num_seqs=wl.B, num_heads=wl.H, tree_size=wl.T,
+                          max_seq_len=wl.max_seq_len + case["bound"], total_kv=wl.total_kv + x,
+                          pool_slots=wl.pool_slots + x, sm_scale=wl.sm_scale, nsplit=case["nsplit"])
+    out = mtv.VerifyAttention(prm)(**dev)
+    torch.cuda.synchronize()
+    got = bf16_out_to_f32(out)
+    assert np.isfinite(got).all()
+    ok, worst, row = parity_gate(got, orc.run(wl))
+    assert ok, f"row {row} at {worst:.2f} bf16 ulp"
