@@ -558,12 +558,14 @@ void verify_attn_partial_kernel(PartialArgs a) {
     return smem_base + (t % NBUF) * TILE_BYTES + wave * (ROWS_PER_LOAD_WAVE * 128);
   };
 
-  // Prologue loads, oldest first: the tree's parent pointers (wave 0) and the
-  // slot entries of tiles 0 and 1 (lane: row lane/8 of this wave's 8); the
-  // first half of this wave's query block into LDS; once the slot entries are
-  // in, the gathers of tiles 0 and 1; then the second half of the query block.
-  int parent = -1;
-  if (wave == 0 && lane < a.T) parent = a.tree_parent[(int64_t)loc.b * a.T + lane];
+  // Prologue loads, oldest first: the tree's parent pointers (wave 0, into
+  // the ancestor-mask array, lane l at byte 4 l; lanes past T repeat node
+  // T-1) and the slot entries of tiles 0 and 1 (lane: row lane/8 of this
+  // wave's 8); the first half of this wave's query block into LDS; once the
+  // slot entries are in, the gathers of tiles 0 and 1; then the second half
+  // of the query block.
+  const uint32_t anc_base = lds_addr(anc_s);
+  if (wave == 0) load_to_lds4(a.tree_parent + (int64_t)loc.b * a.T + min(lane, a.T - 1), anc_base);
   int s_pro[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) s_pro[t] = *slot_ptr(k0 + t * NK, lane >> 3);
@@ -588,12 +590,18 @@ void verify_attn_partial_kernel(PartialArgs a) {
   // r + 16 on positions that differ in bit 0 (the rules of swz above).
   const uint32_t qstage = smem_base + 2 * TILE_BYTES + wave * QSTAGE_BYTES;
   auto qswz = [](int r) { return ((r >> 1) & 3) ^ ((r >> 4) & 1); };
-  // Loads whose first row is past M are skipped (they would only repeat row
-  // 0; the waits below count younger loads only, so they just get looser).
+  // A load whose first row is past M is replaced by zeros written to its
+  // staging slots (the waits below count younger loads only, so they just
+  // get looser). Rows past M in the other loads repeat row 0. Either way a
+  // row past M only feeds its own scores, weights and output column, which
+  // are never stored.
   auto q_stage = [&](int half) {
 #pragma unroll
     for (int j = 0; j < QSTAGE_LOADS; ++j) {
-      if (row0 + (j * 64) / QSTAGE_PIECES >= a.M) continue;  // wave-uniform
+      if (row0 + (j * 64) / QSTAGE_PIECES >= a.M) {  // wave-uniform
+        *(LDS_AS u32x4*)(uintptr_t)(qstage + j * 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+        continue;
+      }
       const int slot = j * 64 + lane;
       const int r = slot / QSTAGE_PIECES;
       const int p = (slot - r * QSTAGE_PIECES) ^ qswz(r);
@@ -607,13 +615,11 @@ void verify_attn_partial_kernel(PartialArgs a) {
 #pragma unroll
     for (int k = 0; k < QK_STEPS / 2; ++k) {
       const int p = 2 * k + hl;
-      u32x4 v = __builtin_bit_cast(u32x4, lds_read_b128(qstage + (r * QSTAGE_PIECES + (p ^ qswz(r))) * 16));
-      if (!row_ok) v = u32x4{0u, 0u, 0u, 0u};
-      qf[half * (QK_STEPS / 2) + k] = __builtin_bit_cast(bf16x8, v);
+      qf[half * (QK_STEPS / 2) + k] = lds_read_b128(qstage + (r * QSTAGE_PIECES + (p ^ qswz(r))) * 16);
     }
   };
-  // A wave without query rows skips the staging loads (its reads are then
-  // replaced by zeros above; the waits below only get looser).
+  // A wave without query rows skips the staging loads (the waits below only
+  // get looser).
   if (wave_active) q_stage(0);
 
   if constexpr (ONE_SEQ) {
@@ -653,16 +659,18 @@ void verify_attn_partial_kernel(PartialArgs a) {
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 7, 0));  // read out before the second half lands
   asm volatile("" ::: "memory");
   if (wave_active) q_stage(1);
-  wait_vmcnt<0>();  // second query half, and with it tiles 0 and 1, landed
-  asm volatile("" ::: "memory");
-  q_read(1);
 
-  // Ancestor masks of this sequence's tree (bit u of anc[t]: node u is t or an
-  // ancestor of t), by pointer jumping over the lanes of wave 0: after round k
-  // a node's mask holds its ancestors within distance 2^(k+1) - 1, and up[t]
-  // is its ancestor at distance 2^(k+1) (or -1). Six rounds cover depth 63.
-  // Parent pointers outside [-1, t-1] make t a root.
+  // While the second half and tiles 0 and 1 land (work kept off the path
+  // from their arrival to the first MFMA):
+  // - Ancestor masks of this sequence's tree (bit u of anc[t]: node u is t or
+  //   an ancestor of t), by pointer jumping over the lanes of wave 0: after
+  //   round k a node's mask holds its ancestors within distance 2^(k+1) - 1,
+  //   and up[t] is its ancestor at distance 2^(k+1) (or -1). Six rounds cover
+  //   depth 63. Parent pointers outside [-1, t-1] make t a root. The parent
+  //   pointers landed with the first query half (they are older loads); every
+  //   lane reads its pointer before the masks overwrite the array.
   if (wave == 0) {
+    const int parent = *(const LDS_AS int*)(uintptr_t)(anc_base + 4 * lane);
     int up = (parent >= 0 && parent < lane && lane < a.T) ? parent : -1;
     unsigned long long m = lane < a.T ? (1ull << lane) : 0ull;
 #pragma unroll
@@ -677,6 +685,18 @@ void verify_attn_partial_kernel(PartialArgs a) {
     }
     if (lane < a.T) anc_s[lane] = m;
   }
+  // - O = 0 in its AGPRs (the empty asm statements make the zeros exist here).
+  f32x16 o[PV_BLOCKS];
+#pragma unroll
+  for (int cb = 0; cb < PV_BLOCKS; ++cb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[cb][i] = 0.f;
+    asm volatile("" : "+a"(o[cb]));
+  }
+
+  wait_vmcnt<0>();  // second query half, and with it tiles 0 and 1, landed
+  asm volatile("" ::: "memory");
+  q_read(1);
 
   // Operand read offsets inside a tile (the chunk group is added as a constant).
   //  QK k-step ks reads chunk 2 ks + l/32 of key row l%32: group ks/4,
@@ -706,11 +726,6 @@ void verify_attn_partial_kernel(PartialArgs a) {
         }
   }
 
-  f32x16 o[PV_BLOCKS];
-#pragma unroll
-  for (int cb = 0; cb < PV_BLOCKS; ++cb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[cb][i] = 0.f;
   float m_run = -INFINITY;  // running reference max (base-2 scaled scores)
   float l_run = 0.f;        // this lane's share of the running sum
 
