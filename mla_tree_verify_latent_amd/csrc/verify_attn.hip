@@ -521,8 +521,8 @@ void verify_attn_partial_kernel(PartialArgs a) {
   int k1 = min(k0 + a.chunk, loc.len);
   int P = loc.len - a.T;
   if constexpr (ONE_SEQ) {
-    // vector loads (a uniform address): their wait is counted with the
-    // prologue's other loads
+    // uniform addresses (the compiler loads both through the scalar cache);
+    // the first use, after the first query loads are issued, waits for them
     len_first = a.seq_lens[0];
     slot_first = a.slot_idx[k0 < a.total_kv ? k0 : a.total_kv - 1];
   }
