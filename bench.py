@@ -388,7 +388,9 @@ def summarize(args):
     }
     if args.sq:
         # SQ counters of the same kernel: MFMA busy cycles (summed over the 1,024
-        # SIMDs) over GRBM_GUI_ACTIVE (summed over the 8 XCDs) -> busy fraction
+        # SIMDs) over GRBM_GUI_ACTIVE (summed over the 8 XCDs) -> busy fraction.
+        # GRBM_GUI_ACTIVE counts the profiled dispatch's window, not shader cycles of
+        # the traced kernel time, so this share is approximate.
         sq, _ = _read_counter_csv(args.sq, "verify_attn_partial")
         out["mfma_busy_frac"] = sq["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / (sq["GRBM_GUI_ACTIVE"] / 8)
         out["lds_bank_conflict_cycles"] = sq["SQ_LDS_BANK_CONFLICT"]
